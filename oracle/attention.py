@@ -1,0 +1,119 @@
+"""Exact scaled-dot-product attention, float64, CPU.  TEST INFRASTRUCTURE ONLY.
+
+What it computes, and where that comes from:
+
+* The FlashAttention v1 post (DeepSchool #630), section «Проблема базового
+  attention», describes standard attention as forming the whole n x n matrix
+  Q K^T and applying a softmax to it.  Its formula images were not captured,
+  so this module takes the textbook reading that the rest of the page
+  supports:  O = softmax(scale * Q K^T [+ causal mask]) V, softmax along each
+  row (over keys).
+* Section «Онлайн-Softmax» of the same post defines the softmax denominator
+  as the row sum of exponentials, and states that the tiled method gives a
+  result fully equivalent to this classic softmax.  So the oracle is the
+  classic form, written out: pass 1 takes the row maximum, pass 2
+  exponentiates the shifted scores, sums them and normalises.  The maximum
+  only guards against overflow; it cancels mathematically.
+* The per-row log-sum-exp LSE_i = m_i + ln(l_i) (natural log) is the one
+  extra output the forward pass writes besides O.  The pages do not mention
+  it; it is the log of the softmax denominator of the *scaled, masked*
+  scores.
+* Causal mask: query i attends to keys j <= i (one shared length N, so
+  top-left and bottom-right alignment coincide).
+* Grouped-query attention: H query heads share Hkv key/value heads in
+  contiguous groups, query head h reads KV head h // (H // Hkv).  The pages
+  only raise GQA as a question (FlashAttention-3 summary, section
+  «Comentários no Hacker News»).
+* A row with no visible key (impossible with the causal mask, since key 0 is
+  always visible) is defined here as O = 0, LSE = -inf.
+
+Parity status: pinned by tests/test_oracle_attention.py against a scalar
+brute-force triple loop, torch's float64 CPU attention routine, closed forms
+(zero queries, constant values, single visible key) and invariances (key
+permutation, key shift, GQA = repeated-KV MHA), and against hand-derived
+values in tests/golden/.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    """Upcast any float array (fp32, or bf16 values already widened to fp32)
+    to float64.  Widening is exact."""
+    return np.asarray(x, dtype=np.float64)
+
+
+def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
+          causal: bool, scale: float):
+    """One (batch, head): qh [N,d], kh/vh [N,d], rows = query indices.
+    Returns O [len(rows), d] and LSE [len(rows)] in float64."""
+    n_keys = kh.shape[0]
+    # Scores for the selected query rows against every key: the full row of
+    # the n x n matrix Q K^T, times the scale.
+    s = scale * (qh[rows] @ kh.T)                       # [R, N]
+    if causal:
+        key_idx = np.arange(n_keys)[None, :]
+        s = np.where(key_idx <= rows[:, None], s, -np.inf)
+    # Pass 1: row maximum over visible keys.
+    m = s.max(axis=1)                                   # [R]
+    dead = ~np.isfinite(m)                              # no visible key
+    m_safe = np.where(dead, 0.0, m)
+    # Pass 2: exponentials of the shifted scores, their sum, normalisation.
+    e = np.exp(s - m_safe[:, None])                     # exp(-inf) = 0
+    l = e.sum(axis=1)                                   # [R]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = e / l[:, None]
+    o = p @ vh                                          # [R, d]
+    lse = m_safe + np.log(l)
+    o[dead] = 0.0
+    lse[dead] = -np.inf
+    return o, lse
+
+
+def attention_rows(q, k, v, rows, *, causal: bool = False, scale=None,
+                   heads=None):
+    """Attention for a subset of query rows.
+
+    q: [B, H, N, d]; k, v: [B, Hkv, N, d]; rows: 1-D int array of query
+    indices (the same rows for every head); heads: optional list of
+    (b, h) pairs to evaluate (default: all).
+
+    Returns (O, LSE) with O: [len(heads), len(rows), d], LSE:
+    [len(heads), len(rows)], float64.  Each output row depends only on its
+    own query and on all keys/values, so evaluating a subset is exact.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, H, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch between q and k/v")
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("H must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    group = H // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    o = np.zeros((len(heads), len(rows), d))
+    lse = np.zeros((len(heads), len(rows)))
+    for i, (b, h) in enumerate(heads):
+        kvh = h // group
+        o[i], lse[i] = _head(q[b, h], k[b, kvh], v[b, kvh], rows, causal,
+                             float(scale))
+    return o, lse
+
+
+def attention(q, k, v, *, causal: bool = False, scale=None):
+    """Full attention.  q: [B,H,N,d]; k, v: [B,Hkv,N,d] (any float dtype).
+
+    Returns O [B,H,N,d] and LSE [B,H,N], both float64.  scale=None means
+    1/sqrt(d)."""
+    q = _as_f64(q)
+    B, H, N, d = q.shape
+    o, lse = attention_rows(q, k, v, np.arange(N), causal=causal, scale=scale)
+    return o.reshape(B, H, N, d), lse.reshape(B, H, N)
