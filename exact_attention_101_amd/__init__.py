@@ -1,0 +1,179 @@
+"""MI355X (gfx950) FlashAttention forward: thin Python binding of libfa.so.
+
+Every step of the computation runs in the HIP kernels of libfa.so; this
+module only checks tensor metadata, allocates outputs with torch (device
+memory) and passes pointers plus torch's current HIP stream through ctypes.
+There is no fallback: if libfa.so is missing or cannot be loaded, every call
+raises.
+
+    o, lse = forward(q, k, v, causal=False, scale=None)
+    q8, amax_descale = quantize_fp8(x, signs=None)
+    o, lse = forward_fp8(q8, k8, v8, descale_qkv, causal=False, scale=None)
+
+Shapes: q [B, H, N, d], k/v [B, Hkv, N, d] (contiguous), o like q (bf16),
+lse [B, H, N] (fp32, natural log).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["forward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+           "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP8_E4M3 = 1
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_MISALIGNED = 3
+FA_ERR_HIP = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-OK status from libfa.so."""
+
+
+def library() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                f"{lib_path} is not built; run "
+                "`python -m exact_attention_101_amd.build` first")
+        lib = ctypes.CDLL(lib_path)
+        vp, i32, f32, i64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_longlong)
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                               i32, f32, i32, vp]
+        lib.fa_fwd.restype = i32
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                   i32, i32, f32, vp, vp]
+        lib.fa_fwd_fp8.restype = i32
+        lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i64, i32, vp, vp]
+        lib.fa_fp8_quantize.restype = i32
+        lib.fa_status_string.argtypes = [i32]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_last_hip_error.argtypes = []
+        lib.fa_last_hip_error.restype = i32
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status == FA_OK:
+        return
+    lib = library()
+    msg = lib.fa_status_string(status).decode()
+    if status == FA_ERR_HIP:
+        raise FaError(f"{msg} (hipError {lib.fa_last_hip_error()})")
+    raise ValueError(msg)
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shape_check(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H(kv), N, d]")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("q, k, v must be on the same GPU")
+    return B, H, k.shape[1], N, d
+
+
+def forward(q, k, v, *, causal: bool = False, scale=None, out=None,
+            lse=None):
+    """bf16 attention forward.  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    import torch
+    B, H, Hkv, N, d = _shape_check(q, k, v)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or \
+            v.dtype != torch.bfloat16:
+        raise ValueError("forward expects bfloat16 q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(library().fa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
+        FA_DTYPE_BF16, _stream_handle(q.device)))
+    return out, lse
+
+
+def forward_fp8(q8, k8, v8, descale_qkv=None, *, causal: bool = False,
+                scale=None, out=None, lse=None):
+    """e4m3 attention forward.  q8/k8/v8: torch.float8_e4m3fn or uint8 codes;
+    descale_qkv: device float32 tensor of 3 descales (or None for 1).
+    Returns (o bf16, lse fp32)."""
+    import torch
+    B, H, Hkv, N, d = _shape_check(q8, k8, v8)
+    for t in (q8, k8, v8):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise ValueError("forward_fp8 expects float8_e4m3fn/uint8 codes")
+    if descale_qkv is not None:
+        if descale_qkv.dtype != torch.float32 or descale_qkv.numel() != 3 or \
+                not descale_qkv.is_cuda or not descale_qkv.is_contiguous():
+            raise ValueError("descale_qkv must be a contiguous float32 CUDA "
+                             "tensor of 3 elements")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check(library().fa_fwd_fp8(
+        q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
+        descale_qkv.data_ptr() if descale_qkv is not None else None,
+        _stream_handle(q8.device)))
+    return out, lse
+
+
+def quantize_fp8(x, signs=None, *, out=None, amax_descale=None):
+    """Per-tensor e4m3 quantisation of a contiguous float32 CUDA tensor whose
+    last dimension is 128, with an optional +-1 sign vector for the Hadamard
+    rotation.  Returns (codes as torch.float8_e4m3fn, amax_descale float32
+    [2] = {amax, descale})."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("quantize_fp8 expects a contiguous float32 CUDA tensor")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if amax_descale is None:
+        amax_descale = torch.empty(2, dtype=torch.float32, device=x.device)
+    sign_buf = None
+    if signs is not None:
+        import numpy as np
+        s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8).reshape(-1))
+        if s.shape[0] != d:
+            raise ValueError("signs must have length d")
+        sign_buf = s
+    _check(library().fa_fp8_quantize(
+        x.data_ptr(), out.data_ptr(), amax_descale.data_ptr(), rows, d,
+        sign_buf.ctypes.data if sign_buf is not None else None,
+        _stream_handle(x.device)))
+    return out.view(torch.float8_e4m3fn), amax_descale

@@ -1,0 +1,53 @@
+"""Build libfa.so in-tree with hipcc for gfx950.
+
+Usage: python -m exact_attention_101_amd.build [--verbose]
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa.so")
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_quant.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-fvisibility=hidden",
+    # Keep the compiler from forming packed fp32 VALU ops.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libfa.so (always rebuilds)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so.
+    noise = ("packed-fp32-ops", "is not a recognized feature")
+    lines = [ln for ln in (res.stdout + res.stderr).splitlines()
+             if ln.strip() and not any(n in ln for n in noise)]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

@@ -1,0 +1,154 @@
+// C ABI of libfa.so: argument validation, kernel selection and launch on the
+// caller's stream.  Declarations and the contract live in include/fa.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_common.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace fa {
+hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
+hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
+                               long long rows, uint64_t sign_lo,
+                               uint64_t sign_hi, bool rotate,
+                               hipStream_t stream);
+}  // namespace fa
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Checks shared by both forward entry points, in the documented order.
+int check_fwd(const void* q, const void* k, const void* v, const void* o,
+              const void* lse, int B, int H, int Hkv, int N, int d,
+              int causal, float scale, int d_ok) {
+  (void)causal;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  // Element counts must fit comfortably in 64 bits; B*H*N must fit in int
+  // arithmetic on the device side (per-head offsets are 64-bit).
+  const long long bhn = static_cast<long long>(B) * H * N;
+  if (bhn > (1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
+  if (!d_ok) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_MISALIGNED;
+  return FA_OK;
+}
+
+fa::FwdArgs make_args(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int H, int Hkv, int N, float scale) {
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.descale = nullptr;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.group = H / Hkv;
+  a.scale = scale;
+  a.neg = scale < 0.f;
+  a.c = fabsf(scale) * 1.4426950408889634f;   // log2(e)
+  return a;
+}
+
+}  // namespace
+
+FA_EXPORT int fa_fwd(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int H, int Hkv, int N, int d,
+                     int causal, float scale, int dtype, void* stream) {
+  if (dtype == FA_DTYPE_FP8_E4M3) {
+    return fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, nullptr,
+                      stream);
+  }
+  const int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale,
+                           dtype == FA_DTYPE_BF16 && (d == 64 || d == 128));
+  if (st != FA_OK) return st;
+  fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Hkv, N, scale);
+  return hip_status(fa::launch_fwd_bf16(a, d, causal != 0,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                         void* o, float* lse, int B, int H, int Hkv, int N,
+                         int d, int causal, float scale,
+                         const float* descale_qkv, void* stream) {
+  const int st = check_fwd(q8, k8, v8, o, lse, B, H, Hkv, N, d, causal, scale,
+                           d == 128);
+  if (st != FA_OK) return st;
+  if (descale_qkv && (reinterpret_cast<uintptr_t>(descale_qkv) & 3u))
+    return FA_ERR_MISALIGNED;
+  fa::FwdArgs a = make_args(q8, k8, v8, o, lse, B, H, Hkv, N, scale);
+  a.descale = descale_qkv;
+  return hip_status(
+      fa::launch_fwd_fp8(a, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,
+                              long long rows, int d,
+                              const signed char* signs_host, void* stream) {
+  if (!x || !x8 || !amax_descale) return FA_ERR_INVALID_ARGUMENT;
+  if (rows <= 0 || d <= 0 || rows > (1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
+  uint64_t lo = 0, hi = 0;
+  if (signs_host) {
+    for (int i = 0; i < d && i < 128; ++i) {
+      const int s = signs_host[i];
+      if (s != 1 && s != -1) return FA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(x8) ||
+      (reinterpret_cast<uintptr_t>(amax_descale) & 3u))
+    return FA_ERR_MISALIGNED;
+  if (signs_host) {
+    for (int i = 0; i < 128; ++i) {
+      if (signs_host[i] < 0) {
+        if (i < 64) lo |= (1ULL << i);
+        else hi |= (1ULL << (i - 64));
+      }
+    }
+  }
+  return hip_status(fa::launch_fp8_quantize(
+      x, static_cast<uint8_t*>(x8), amax_descale, rows, lo, hi,
+      signs_host != nullptr, static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARGUMENT:
+      return "FA_ERR_INVALID_ARGUMENT: null pointer, non-positive size, H not "
+             "a multiple of Hkv, non-finite scale or oversized tensor";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dimension or dtype not supported";
+    case FA_ERR_MISALIGNED:
+      return "FA_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch failed";
+    default: return "unknown fa status";
+  }
+}
+
+FA_EXPORT int fa_last_hip_error(void) { return g_last_hip_error; }
+
+FA_EXPORT int fa_version(void) { return 100; }

@@ -1,0 +1,75 @@
+// Shared device helpers and launch descriptors for the gfx950 attention
+// kernels.  Internal header (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// Arguments of one forward launch.  Element strides are 64-bit.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* descale;   // fp8 only: {dQ, dK, dV} or nullptr
+  int B, H, Hkv, N;
+  int group;              // H / Hkv
+  int nqb;                // number of query blocks
+  float c;                // |scale| * log2(e): scores enter exp2 in log2 units
+  float scale;            // signed scale (fp8 path folds descales into it)
+  int neg;                // scale < 0: Q is negated on load so that c >= 0
+  int xcd_chunk;          // 1: map workgroups to XCD-contiguous work ranges
+};
+
+// Within a 32-row MFMA block, swap bits 2 and 3 of the row index.  Loading
+// the A operand of S^T = K Q^T with key rows in this order makes every lane
+// of the 32x32 accumulator hold 8 consecutive keys per half (keys 8h..8h+7
+// and 16+8h..16+8h+7 of the block for lane half h), which is exactly the
+// k-ordering the B operand of the following P V product wants.  It is an
+// involution.
+__device__ __forceinline__ int sigma(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Work-unit mapping.  Workgroup ids are dispatched round-robin over the 8
+// XCDs (id % 8), each with its own L2.  Give each XCD a contiguous range of
+// work so the query blocks that share one (batch, KV head) run on the same
+// XCD and reuse K/V from its L2.  Causal launches go heaviest query block
+// first (longest-processing-time order) inside each XCD's range.
+__device__ __forceinline__ void map_work(int L, int T, int BH, int nqb,
+                                         bool causal, int xcd_chunk, int& bh,
+                                         int& qb) {
+  if (xcd_chunk) {
+    const int per = T >> 3;
+    const int x = L & 7;
+    const int s = L >> 3;
+    if (causal) {
+      const int hpx = BH >> 3;           // heads per XCD (BH % 8 == 0)
+      bh = x * hpx + s % hpx;
+      qb = nqb - 1 - s / hpx;
+    } else {
+      const int W = x * per + s;
+      bh = W / nqb;
+      qb = W % nqb;
+    }
+  } else {
+    if (causal) {
+      bh = L % BH;
+      qb = nqb - 1 - L / BH;
+    } else {
+      bh = L / nqb;
+      qb = L % nqb;
+    }
+  }
+}
+
+}  // namespace fa

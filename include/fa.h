@@ -1,0 +1,143 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention forward library
+ * (libfa.so).
+ *
+ * The operation.  Exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * softmax over keys, computed the FlashAttention way: Q is split into row
+ * blocks, the K/V blocks stream past each one through on-chip memory, and an
+ * online softmax keeps a running row maximum, a running denominator and a
+ * running output that is rescaled whenever the maximum grows, so the N x N
+ * score matrix never reaches device memory.  Sources: the FlashAttention v1
+ * post (DeepSchool #630), sections «Проблема базового attention» (the
+ * operation and the cost of materialising Q K^T), «Тайлинг (Tiling)» (row
+ * blocks of Q against streamed K/V blocks), «Онлайн-Softmax» (running max,
+ * running denominator, rescale of the partial output) and «Итог» (linear
+ * memory); the FlashAttention-3 summary (GeekNews), section «Resumo do
+ * FlashAttention» (the attention matrix is never written out).  Besides O
+ * the forward writes the per-row natural-log log-sum-exp LSE of the scaled,
+ * masked scores, the only other output.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are HIP device allocations owned by the caller.  The
+ *     library never allocates or frees device memory, never synchronises the
+ *     device, and holds no mutable global state; calls are thread-safe.
+ *   - Layouts are dense row-major:  q, o: [B][H][N][d];  k, v: [B][Hkv][N][d];
+ *     lse: [B][H][N] (float, natural log).  All offsets are 64-bit.
+ *   - Grouped-query attention: H must be a multiple of Hkv; query head h
+ *     reads key/value head h / (H / Hkv).
+ *   - causal != 0 hides key j from query i when j > i.
+ *   - Work is only enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Errors raised while a kernel runs surface at the caller's
+ *     next synchronisation.
+ *   - Outputs are fully overwritten; inputs are never written.  Outputs must
+ *     not alias inputs.
+ *   - Return value: an fa_status_t.  Arguments are checked in this order and
+ *     the first failure is returned before anything is enqueued:
+ *       FA_ERR_INVALID_ARGUMENT  null pointer, B/H/Hkv/N/d <= 0, H % Hkv != 0,
+ *                                non-finite scale, sizes whose element
+ *                                counts overflow 64 bits;
+ *       FA_ERR_UNSUPPORTED       d not supported by the kernel family, or an
+ *                                unknown dtype;
+ *       FA_ERR_MISALIGNED        a tensor pointer not 16-byte aligned;
+ *       FA_ERR_HIP               the launch failed (fa_last_hip_error() gives
+ *                                the hipError_t).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_BF16 = 0,      /* q, k, v, o: bfloat16 */
+  FA_DTYPE_FP8_E4M3 = 1   /* q, k, v: OCP e4m3 ("e4m3fn") codes; o: bfloat16 */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_MISALIGNED = 3,
+  FA_ERR_HIP = 4
+} fa_status_t;
+
+/*
+ * fa_fwd -- attention forward.
+ *   q, k, v  device, dtype as below, layouts as above (read only).
+ *   o        device, bfloat16 [B][H][N][d] (written).
+ *   lse      device, float [B][H][N] (written): ln sum_j exp(scale*q_i.k_j)
+ *            over the visible keys j.
+ *   B, H, Hkv, N, d   sizes; d in {64, 128} for bf16, d == 128 for fp8.
+ *                     Any N >= 1 (ragged tails are masked).
+ *   causal   0 or non-zero (lower-triangular: key j <= query i).
+ *   scale    multiplies Q K^T; any finite value (0 and negative included).
+ *   dtype    fa_dtype_t.  FA_DTYPE_FP8_E4M3 here means all three descale
+ *            factors are 1; use fa_fwd_fp8 to pass per-tensor descales.
+ *   stream   hipStream_t or NULL.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int N, int d, int causal, float scale,
+           int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on per-tensor-scaled OCP e4m3 inputs, the
+ * FP8 path of the FlashAttention-3 summary (GeekNews), sections «Principais
+ * tecnologias do FlashAttention-3» and «Novos recursos de hardware da GPU
+ * Hopper»: tensor X is represented by codes x8 and a descale factor
+ * delta_X with X ~= decode(x8) * delta_X.
+ *   q8, k8, v8   device e4m3 codes, layouts as above.
+ *   o, lse       as for fa_fwd (o is bfloat16).
+ *   descale_qkv  device float[3] = {delta_Q, delta_K, delta_V}, read by the
+ *                kernel (no host synchronisation), or NULL for {1, 1, 1}.
+ *   d            must be 128.  Other arguments as for fa_fwd.
+ * Computes O = softmax(scale * dQ * dK * Q8 K8^T) (dV * V8) with Q8/K8/V8 the
+ * decoded codes; P is rounded to e4m3 before the P V product.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o,
+               float* lse, int B, int H, int Hkv, int N, int d, int causal,
+               float scale, const float* descale_qkv, void* stream);
+
+/*
+ * fa_fp8_quantize -- optional random-sign Hadamard rotation of each row, then
+ * per-tensor OCP e4m3 quantisation ("incoherent processing" of the
+ * FlashAttention-3 summary, section «Baixa precisão: redução do erro de
+ * quantização com processamento incoerente»).
+ *   x             device float [rows][d] (read only).
+ *   x8            device uint8 [rows][d] (written): e4m3 codes of
+ *                 x' * (448 / amax), rounded to nearest even in fp32 and
+ *                 saturated to +-448, where x' = x diag(s) H_d / sqrt(d) if
+ *                 signs are given (H_d the Sylvester Hadamard matrix) and
+ *                 x' = x otherwise, and amax = max |x'| over the tensor.
+ *   amax_descale  device float[2] (written): {amax, amax / 448}; amax = 0
+ *                 gives a descale of 1.  Element 1 is the delta to pass to
+ *                 fa_fwd_fp8.
+ *   rows, d       rows >= 1, d == 128.
+ *   signs_host    host array of d int8 values, each +1 or -1, or NULL for no
+ *                 rotation.  Q and K must be rotated with the same signs (the
+ *                 rotation is orthonormal, so Q K^T is unchanged); V is not
+ *                 rotated.
+ *   stream        hipStream_t or NULL.  Three kernels are enqueued in order:
+ *                 clear amax, reduce amax, quantise.
+ * Errors as listed above; signs other than +-1 give FA_ERR_INVALID_ARGUMENT.
+ */
+int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,
+                    long long rows, int d, const signed char* signs_host,
+                    void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/* hipError_t behind the most recent FA_ERR_HIP returned on this thread
+ * (0 if none). */
+int fa_last_hip_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,47 @@
+"""Shared helpers of the GPU parity tests (not a test module)."""
+
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import workloads
+
+BF16_O_TOL = 2e-2      # max |O_gpu - O_oracle|
+LSE_TOL = 1e-3         # max |LSE_gpu - LSE_oracle|
+FP8_REL_L2_TOL = 5e-2  # ||O_gpu - O_ref|| / ||O_ref|| on dequantised inputs
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+@functools.lru_cache(maxsize=2)
+def bf16_inputs(name: str):
+    """Seeded bf16 inputs of a named workload: (q, k, v) as torch bf16 CPU
+    tensors plus the exact values as float32 numpy arrays."""
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.workload_qkv(w)
+    tb = tuple(workloads.to_bf16(x) for x in (q, k, v))
+    return tb, tuple(workloads.bf16_values(t) for t in tb)
+
+
+def sample_rows(N: int, seed: int, n_random: int = 24):
+    """Query rows checked at full size: the first and last rows, rows around
+    the 64/128/256 block boundaries, and random rows."""
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, N // 2,
+             N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, N, n_random)
+    rows = sorted({int(r) for r in list(fixed) + list(rnd) if 0 <= r < N})
+    return np.array(rows, dtype=np.int64)
+
+
+def sample_heads(B: int, H: int, seed: int, n: int = 6):
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (B - 1, H - 1)}
+    while len(heads) < min(n, B * H):
+        heads.add((int(rng.integers(0, B)), int(rng.integers(0, H))))
+    return sorted(heads)

@@ -1,0 +1,109 @@
+"""The C-ABI library loads without a GPU, exports every entry point that
+include/fa.h declares, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_101_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path):
+        from exact_attention_101_amd import build
+        build.build()
+    return fa.library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_fp8_quantize", "fa_status_string",
+              "fa_last_hip_error", "fa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_version() == 100
+    for s in range(0, 6):
+        assert lib.fa_status_string(s)
+    assert lib.fa_last_hip_error() == 0
+
+
+# Fake, never-dereferenced device addresses: validation must fail before any
+# HIP call.
+A = 0x10000          # 16-byte aligned
+M = 0x10008          # misaligned
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=2, Hkv=2, N=8, d=128,
+         causal=0, scale=0.1, dtype=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, dtype,
+                      None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None),
+                                dict(o=None), dict(lse=None), dict(B=0),
+                                dict(H=0), dict(Hkv=0), dict(N=0), dict(d=0),
+                                dict(N=-3), dict(H=6, Hkv=4),
+                                dict(scale=float("nan")),
+                                dict(scale=float("inf")),
+                                dict(B=1 << 20, H=1 << 20, N=1 << 10)])
+def test_invalid_arguments(lib, kw):
+    assert _fwd(lib, **kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(d=32),
+                                dict(dtype=7)])
+def test_unsupported(lib, kw):
+    assert _fwd(lib, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fp8_only_d128(lib):
+    assert _fwd(lib, d=64, dtype=1) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_fp8(A, A, A, A, A, 1, 1, 1, 8, 64, 0, 0.1, None,
+                          None) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_misaligned(lib, which):
+    assert _fwd(lib, **{which: M}) == fa.FA_ERR_MISALIGNED
+
+
+def test_invalid_before_unsupported_before_misaligned(lib):
+    assert _fwd(lib, q=M, d=96, N=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _fwd(lib, q=M, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_quantize_validation(lib):
+    signs = (ctypes.c_int8 * 128)(*([1] * 128))
+    bad = (ctypes.c_int8 * 128)(*([1] * 127 + [0]))
+    q = lib.fa_fp8_quantize
+    assert q(None, A, A, 4, 128, None, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert q(A, A, A, 0, 128, None, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert q(A, A, A, 4, 128, bad, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert q(A, A, A, 4, 64, None, None) == fa.FA_ERR_UNSUPPORTED
+    assert q(M, A, A, 4, 128, signs, None) == fa.FA_ERR_MISALIGNED
+
+
+def test_python_wrapper_raises_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x)

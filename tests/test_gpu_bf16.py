@@ -1,0 +1,167 @@
+"""Parity of the bf16 HIP forward against the CPU fp64 oracle, called
+through the C ABI (exact_attention_101_amd.forward -> fa_fwd)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import (BF16_O_TOL, LSE_TOL, bf16_inputs, dev, sample_heads,
+                         sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(qb, kb, vb, causal, scale=None):
+    import torch
+    import exact_attention_101_amd as fa
+    d = dev()
+    o, lse = fa.forward(qb.to(d), kb.to(d), vb.to(d), causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(o, lse, ro, rl, tol=BF16_O_TOL):
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    eo = float(np.abs(o - ro).max())
+    el = float(np.abs(lse - rl).max())
+    print(f"max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= tol, eo
+    assert el <= LSE_TOL, el
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_full(causal):
+    (qb, kb, vb), (q, k, v) = bf16_inputs("tiny_d64")
+    o, lse = _run(qb, kb, vb, causal)
+    ro, rl = oracle.attention(q, k, v, causal=causal)
+    _check(o, lse, ro, rl)
+
+
+SMALL = [
+    # B, H, Hkv, N, d
+    (1, 1, 1, 1, 64), (1, 1, 1, 1, 128), (1, 2, 1, 17, 128),
+    (2, 2, 2, 100, 64), (1, 4, 2, 255, 128), (1, 2, 2, 257, 128),
+    (2, 4, 1, 300, 64), (1, 3, 3, 513, 128), (1, 8, 2, 1000, 128),
+    (1, 2, 2, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_ragged_full(shape, causal):
+    B, H, Hkv, N, d = shape
+    q, k, v = workloads.qkv(B, H, Hkv, N, d, 4000 + N + d)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    o, lse = _run(*tb, causal)
+    ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb),
+                              causal=causal)
+    _check(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("name", ["bf16_n4096", "bf16_causal_n8192",
+                                  "bf16_causal_gqa_n16384", "bf16_n8192"])
+def test_full_size_sampled(name):
+    """The workloads at full size, in the launch the benchmark times; the
+    oracle evaluates sampled rows of sampled heads one by one."""
+    w = workloads.WORKLOADS[name]
+    (qb, kb, vb), (q, k, v) = bf16_inputs(name)
+    o, lse = _run(qb, kb, vb, w.causal)
+    rows = sample_rows(w.N, w.index)
+    heads = sample_heads(w.B, w.H, w.index)
+    ro, rl = oracle.attention_rows(q, k, v, rows, causal=w.causal, heads=heads)
+    go = np.stack([o[b, h][rows] for b, h in heads])
+    gl = np.stack([lse[b, h][rows] for b, h in heads])
+    _check(go, gl, ro, rl)
+    # properties over the whole output
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(o).max() <= np.abs(v).max()   # convex combination of V rows
+
+
+def test_gqa_equals_repeated_kv_bitwise():
+    import torch
+    q, k, v = workloads.qkv(2, 8, 2, 333, 128, 51)
+    qb, kb, vb = (workloads.to_bf16(x) for x in (q, k, v))
+    for causal in (False, True):
+        o1, l1 = _run(qb, kb, vb, causal)
+        o2, l2 = _run(qb, kb.repeat_interleave(4, dim=1).contiguous(),
+                      vb.repeat_interleave(4, dim=1).contiguous(), causal)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_causal_first_row_is_v0():
+    (qb, kb, vb), (q, k, v) = bf16_inputs("tiny_d64")
+    o, lse = _run(qb, kb, vb, True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    s = np.einsum("bhd,bhd->bh", q[:, :, 0].astype(np.float64),
+                  k[:, :, 0].astype(np.float64)) / math.sqrt(64)
+    np.testing.assert_allclose(lse[:, :, 0], s, atol=LSE_TOL)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(causal):
+    import torch
+    q, k, _ = workloads.qkv(1, 2, 2, 700, 128, 61)
+    c = workloads.to_bf16(np.linspace(-3, 3, 128, dtype=np.float32))
+    vb = c.reshape(1, 1, 1, 128).expand(1, 2, 700, 128).contiguous()
+    o, _ = _run(workloads.to_bf16(q), workloads.to_bf16(k), vb, causal)
+    np.testing.assert_array_equal(
+        o, np.broadcast_to(workloads.bf16_values(c), o.shape))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
+def test_scale_edge_cases(scale):
+    q, k, v = workloads.qkv(1, 2, 2, 200, 64, 71)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    for causal in (False, True):
+        o, lse = _run(*tb, causal, scale=scale)
+        ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb),
+                                  causal=causal, scale=scale)
+        _check(o, lse, ro, rl)
+
+
+def test_key_permutation_noncausal():
+    q, k, v = workloads.qkv(1, 2, 2, 512, 128, 81)
+    perm = np.random.default_rng(0).permutation(512)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    o1, l1 = _run(*tb, False)
+    o2, l2 = _run(tb[0], tb[1][:, :, perm].contiguous(),
+                  tb[2][:, :, perm].contiguous(), False)
+    assert np.abs(o1 - o2).max() <= BF16_O_TOL / 2
+    assert np.abs(l1 - l2).max() <= LSE_TOL
+
+
+def test_deterministic_and_batch_independent():
+    q, k, v = workloads.qkv(2, 4, 4, 777, 128, 91)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    for causal in (False, True):
+        a = _run(*tb, causal)
+        b = _run(*tb, causal)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        one = _run(*(t[1:2].contiguous() for t in tb), causal)
+        assert np.array_equal(a[0][1:2], one[0])
+        assert np.array_equal(a[1][1:2], one[1])
+
+
+def test_outputs_only_written_in_bounds():
+    """Guard bands around O and LSE stay untouched."""
+    import torch
+    import exact_attention_101_amd as fa
+    d = dev()
+    q, k, v = workloads.qkv(1, 2, 2, 130, 128, 101)
+    qb, kb, vb = (workloads.to_bf16(x).to(d) for x in (q, k, v))
+    pad = 4096
+    obuf = torch.full((pad + qb.numel() + pad,), 7.0, dtype=torch.bfloat16,
+                      device=d)
+    lbuf = torch.full((pad + 2 * 130 + pad,), 7.0, dtype=torch.float32,
+                      device=d)
+    o = obuf[pad:pad + qb.numel()].view(qb.shape)
+    lse = lbuf[pad:pad + 260].view(1, 2, 130)
+    for causal in (False, True):
+        fa.forward(qb, kb, vb, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.all(obuf[:pad] == 7.0) and torch.all(obuf[-pad:] == 7.0)
+        assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[-pad:] == 7.0)

@@ -1,0 +1,108 @@
+"""Parity of the fp8 path (GPU quantisation + e4m3 forward) against the CPU
+oracle, through the C ABI (fa_fp8_quantize, fa_fwd_fp8)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import FP8_REL_L2_TOL, LSE_TOL, dev, sample_heads, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant(x, signs=None):
+    import torch
+    import exact_attention_101_amd as fa
+    codes, ad = fa.quantize_fp8(torch.from_numpy(x).to(dev()), signs)
+    torch.cuda.synchronize()
+    return codes, ad
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("rows", [1, 7, 1000, 33000])
+def test_quantize_matches_oracle(rotate, rows):
+    x = workloads.draw((rows, 128), 1234 + rows, outliers=True)
+    signs = workloads.hadamard_signs(128, 9) if rotate else None
+    codes, ad = _quant(x, signs)
+    g = codes.view(__import__("torch").uint8).cpu().numpy()
+    rc, rdesc, ramax = oracle.quantize_per_tensor(x, signs)
+    ad = ad.cpu().numpy()
+    if not rotate:
+        # same fp32 decision on both sides: bit-exact
+        assert ad[0] == ramax and ad[1] == rdesc
+        np.testing.assert_array_equal(g, rc)
+    else:
+        # the GPU rotation rounds in fp32 in its own order; codes may differ
+        # only where x' * inv lies within a few ulps of a rounding boundary
+        assert abs(ad[0] - ramax) <= 4e-6 * ramax
+        diff = g != rc
+        assert diff.mean() <= 1e-3
+        dv = np.abs(oracle.e4m3_decode(g[diff]) - oracle.e4m3_decode(rc[diff]))
+        step = np.maximum(np.abs(oracle.e4m3_decode(rc[diff])) * 2.0 ** -3,
+                          2.0 ** -9)
+        assert np.all(dv <= step * 1.0001)
+
+
+def test_quantize_zero_tensor():
+    codes, ad = _quant(np.zeros((64, 128), np.float32))
+    assert np.all(codes.view(__import__("torch").uint8).cpu().numpy() == 0)
+    np.testing.assert_array_equal(ad.cpu().numpy(), [0.0, 1.0])
+
+
+def _fp8_forward(q, k, v, signs, causal, Hkv=None):
+    import torch
+    import exact_attention_101_amd as fa
+    q8, sq = _quant(q, signs)
+    k8, sk = _quant(k, signs)
+    v8, sv = _quant(v, None)
+    desc = torch.stack([sq[1], sk[1], sv[1]]).contiguous()
+    o, lse = fa.forward_fp8(q8, k8, v8, desc, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _oracle_deq(x, signs):
+    codes, ds, _ = oracle.quantize_per_tensor(x, signs)
+    return oracle.e4m3_decode(codes) * float(ds)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 256), (2, 4, 2, 300), (1, 2, 2, 1),
+                                   (1, 2, 1, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_small_full(shape, causal, rotate):
+    B, H, Hkv, N = shape
+    q, k, v = workloads.qkv(B, H, Hkv, N, 128, 5000 + N, outliers=True)
+    signs = workloads.hadamard_signs(128, 5009) if rotate else None
+    o, lse = _fp8_forward(q, k, v, signs, causal)
+    qd, kd, vd = _oracle_deq(q, signs), _oracle_deq(k, signs), _oracle_deq(v, None)
+    ro, rl = oracle.attention(qd, kd, vd, causal=causal)
+    rel = np.linalg.norm(o - ro) / np.linalg.norm(ro)
+    print(f"fp8 rel-L2={rel:.3e} max|dLSE|={np.abs(lse - rl).max():.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert rel <= FP8_REL_L2_TOL
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fp8_full_size_sampled(rotate):
+    """The fp8 workload at full size; sampled rows of sampled heads against
+    the oracle on the oracle's own dequantised inputs.  Also reports (not
+    gated) the error against the unquantised inputs."""
+    w = workloads.WORKLOADS["fp8_n8192"]
+    q, k, v = workloads.workload_qkv(w)
+    signs = workloads.hadamard_signs(w.d, w.seed(9)) if rotate else None
+    o, lse = _fp8_forward(q, k, v, signs, w.causal)
+    rows = sample_rows(w.N, w.index, n_random=8)
+    heads = sample_heads(w.B, w.H, w.index, n=4)
+    qd, kd, vd = _oracle_deq(q, signs), _oracle_deq(k, signs), _oracle_deq(v, None)
+    ro, rl = oracle.attention_rows(qd, kd, vd, rows, heads=heads)
+    go = np.stack([o[b, h][rows] for b, h in heads])
+    rel = np.linalg.norm(go - ro) / np.linalg.norm(ro)
+    exact, _ = oracle.attention_rows(q, k, v, rows, heads=heads)
+    rel_exact = np.linalg.norm(go - exact) / np.linalg.norm(exact)
+    print(f"fp8 rotate={rotate}: rel-L2 vs dequantised oracle {rel:.3e}; "
+          f"vs unquantised inputs {rel_exact:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert rel <= FP8_REL_L2_TOL
