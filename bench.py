@@ -1,0 +1,251 @@
+"""Benchmark of the MI355X FlashAttention forward.
+
+One step = one bf16 attention forward (fa_fwd through the C ABI) over the
+headline workload: B=4, H=16, N=8192, d=128, non-causal, N(0,1) inputs cast
+to bf16, output bf16 O plus fp32 LSE.  Throughput counts 4*B*H*N^2*d FLOPs
+(halved when causal).  Inputs are resident in device memory before the timed
+region; the timed region is W untimed warm-up steps, then K steps bracketed
+by device synchronisations, timed with HIP events recorded on the stream the
+kernels are launched on.
+
+Prints ONE JSON line (rank 0, one GPU) with the throughput, a roofline object
+for the attention kernel (MFMA-bound; achieved FLOP/s over the dense bf16
+peak), the oracle timed on the host cores on a bounded sample, and secondary
+measurements of the other workloads (causal, GQA, fp8, quantisation).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+FP8_PEAK_TFLOPS = 5033.2    # dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+
+METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, N=8192, d=128, 1 GPU)"
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_101_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != _kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def _time_launches(fn, steps: int, warmup: int):
+    """Average milliseconds per call of fn() over `steps` calls, HIP events
+    on torch's current stream (the stream fn launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def _bf16_workload(name):
+    """Seeded inputs of a named bf16 workload: device bf16 tensors plus the
+    host bf16 tensors they were copied from."""
+    import torch
+    import workloads
+    w = workloads.WORKLOADS[name]
+    host = tuple(workloads.to_bf16(x) for x in workloads.workload_qkv(w))
+    dev = torch.device("cuda:0")
+    return w, tuple(t.to(dev) for t in host), host
+
+
+def _cpu_baseline(w, host, budget_s: float):
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    workload: whole heads (every query row against every key) of the same
+    seeded inputs, as many as fit in the time budget."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()),
+                    default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    qh, kh, vh = host
+    t0 = time.perf_counter()
+    n, secs = 0, 0.0
+    while n < w.B * w.H and time.perf_counter() - t0 < budget_s:
+        b, h = divmod(n, w.H)
+        kvh = h // (w.H // w.Hkv)
+        args = (workloads.bf16_values(qh[b:b + 1, h:h + 1]),
+                workloads.bf16_values(kh[b:b + 1, kvh:kvh + 1]),
+                workloads.bf16_values(vh[b:b + 1, kvh:kvh + 1]))
+        t1 = time.perf_counter()
+        oracle.attention(*args, causal=w.causal)
+        secs += time.perf_counter() - t1
+        n += 1
+    flops = w.flops / (w.B * w.H) * n
+    return {
+        "value": round(flops / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{n} of {w.B * w.H} heads of {w.name} (all {w.N} query "
+                  f"rows of each head, fp64 numpy oracle, {secs:.1f} s); "
+                  "same FLOP convention",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary workloads")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy "
+                         "(reference point for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the forward kernel runs on a "
+              f"single device and this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import exact_attention_101_amd as fa
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w, (q, k, v), host = _bf16_workload(workloads.HEADLINE)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.forward(q, k, v, causal=w.causal, out=o, lse=lse)
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    torch.cuda.synchronize()
+    ms = _time_launches(step, args.steps, args.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+
+    extras = {}
+    if not args.no_extras:
+        for name in ("bf16_n4096", "bf16_causal_n8192",
+                     "bf16_causal_gqa_n16384"):
+            ww, (qq, kk, vv), _ = _bf16_workload(name)
+            oo = torch.empty_like(qq)
+            ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
+                             device=dev)
+            m = _time_launches(lambda: fa.forward(qq, kk, vv, causal=ww.causal,
+                                                  out=oo, lse=ll), 10, 3)
+            t = ww.flops / (m * 1e-3) / 1e12
+            extras[name] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
+                            "frac_of_bf16_peak": round(t / BF16_PEAK_TFLOPS, 4)}
+            del qq, kk, vv, oo, ll
+        ww = workloads.WORKLOADS["fp8_n8192"]
+        xq, xk, xv = (torch.from_numpy(x).to(dev)
+                      for x in workloads.workload_qkv(ww))
+        signs = workloads.hadamard_signs(ww.d, ww.seed(9))
+        for rot in (False, True):
+            s = signs if rot else None
+            q8, sq = fa.quantize_fp8(xq, s)
+            k8, sk = fa.quantize_fp8(xk, s)
+            v8, sv = fa.quantize_fp8(xv, None)
+            desc = torch.stack([sq[1], sk[1], sv[1]]).contiguous()
+            oo = torch.empty((ww.B, ww.H, ww.N, ww.d), dtype=torch.bfloat16,
+                             device=dev)
+            ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
+                             device=dev)
+            m = _time_launches(lambda: fa.forward_fp8(q8, k8, v8, desc,
+                                                      out=oo, lse=ll), 10, 3)
+            t = ww.flops / (m * 1e-3) / 1e12
+            key = "fp8_n8192" + ("_hadamard" if rot else "")
+            extras[key] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
+                           "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
+        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 10, 3)
+        nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
+        extras["fp8_quantize_hadamard_per_tensor"] = {
+            "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    cpu = None
+    if not args.no_cpu and rank == 0:
+        cpu = _cpu_baseline(w, host, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal},
+        "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": _traffic("fwd_bf16_d128"),
+            "kernel": "fwd_bf16_kernel<128, false>",
+            "flops_per_launch": w.flops,
+        },
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "gpu": torch.cuda.get_device_properties(0).name,
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

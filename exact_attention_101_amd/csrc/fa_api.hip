@@ -69,7 +69,10 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, void* o,
   a.group = H / Hkv;
   a.scale = scale;
   a.neg = scale < 0.f;
-  a.c = fabsf(scale) * 1.4426950408889634f;   // log2(e)
+  // Scores enter exp2 as S * c, c = |scale| * log2(e).  c is floored at
+  // 1e-30 so that a masked score (-inf) always gives p = 0; for |scale| that
+  // small every visible score maps to exp2(~0) = 1 in fp32 either way.
+  a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);
   return a;
 }
 

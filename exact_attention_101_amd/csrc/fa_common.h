@@ -30,6 +30,13 @@ struct FwdArgs {
   int xcd_chunk;          // 1: map workgroups to XCD-contiguous work ranges
 };
 
+// x if ok, else zero; selected per 32-bit component (a select of the whole
+// vector can end up in private memory).
+__device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {
+  return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u,
+                    ok ? x.w : 0u);
+}
+
 // Within a 32-row MFMA block, swap bits 2 and 3 of the row index.  Loading
 // the A operand of S^T = K Q^T with key rows in this order makes every lane
 // of the 32x32 accumulator hold 8 consecutive keys per half (keys 8h..8h+7

@@ -14,22 +14,36 @@
 //
 // gfx950 mapping:
 //   * workgroup = 4 waves, BR = 128 query rows (32 per wave), K/V blocks of
-//     BC = 64 keys, double-buffered in LDS;
+//     BC = 64 keys.  K and V blocks go from HBM/L2 straight into LDS with
+//     buffer_load_dwordx4 ... lds (no register staging), into four distinct
+//     LDS stage arrays (two for K, two for V) so the compiler can tell the
+//     in-flight copies from the stages being read;
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: the accumulator column is the query, so each
 //     lane holds 32 scores of one query and the row max / row sum are
-//     in-lane plus one exchange between the two lane halves;
+//     in-lane plus one v_permlane32_swap between the two lane halves;
 //   * Q lives in registers as the B operand for the whole kernel; the
 //     contraction over d is permuted so that lane half h holds the
 //     contiguous d-range [h*D/2, (h+1)*D/2);
-//   * K rows are loaded in sigma order (see fa_common.h), so the fp32 score
+//   * K rows are loaded in sigma order (fa_common.h), so the fp32 score
 //     accumulator, converted to bf16, is directly the B operand of
 //     O^T = V^T P^T; V stays in its [key][d] layout in LDS and the A operand
 //     (V^T) is read with the transposing ds_read_b64_tr_b16;
 //   * softmax in fp32 registers in the log2 domain: p = exp2(S*c - m) with
-//     c = |scale| * log2(e) (one FMA + v_exp_f32 per score);
-//   * LDS rows are XOR-swizzled at 16-byte granularity so the MFMA operand
-//     reads are free of bank conflicts.
+//     c = |scale| * log2(e) (one FMA + v_exp_f32 per score), fp32 row sums;
+//   * the two matrix products overlap the softmax inside each wave (the
+//     intra-group overlap of the FlashAttention-3 summary, section
+//     «Assincronia: sobreposição de GEMM e Softmax»): while the matrix core
+//     computes the scores of block t+1, the vector unit turns the scores of
+//     block t into P; then the P V product of block t runs.  The order is
+//     pinned with scheduling-group barriers;
+//   * the running maximum is only moved when a block's maximum exceeds it by
+//     more than TAU (log2 units).  Any reference value gives the same
+//     softmax (the shift cancels between numerator and denominator), so this
+//     stays exact; it bounds p by 2^TAU and makes the rescale of O rare;
+//   * LDS layouts are chosen so every MFMA operand read is free of bank
+//     conflicts: K rows are padded by one 16-byte slot, V rows XOR their
+//     64-byte segments with the key's position in its group of 4.
 #include "fa_common.h"
 
 namespace fa {
@@ -39,36 +53,43 @@ namespace {
 constexpr int BR = 128;
 constexpr int BC = 64;
 constexpr int NTHR = 256;
-
-// Physical 16-byte chunk of logical chunk c in K-tile row r (D/8 chunks per
-// row).  Lane i of a wave reads row sigma(i) (+32 kb), so the XOR term seen
-// by lane i is a function of i alone: (i & 15) for 16-chunk rows, and
-// (i & 7) ^ ((i >> 3) & 1) for 8-chunk rows.  Either way 8 consecutive lanes
-// (and, for 16-chunk rows, 16) hit distinct bank groups.
-template <int NCH>
-__device__ __forceinline__ int swz(int r, int c) {
-  const int t = sigma(r & 31);
-  if constexpr (NCH == 16) {
-    return c ^ (t & 15);
-  } else {
-    return c ^ ((t & 7) ^ ((t >> 3) & 1));
-  }
-}
-
-// V tile: row = key, 64-byte segments of the row are XOR-ed with the key's
-// position inside its group of 4 (16-chunk rows) or with bit 1 of the key
-// (8-chunk rows), so the 4 key rows read by one ds_read_b64_tr_b16 land in
-// different banks.
-template <int NCH>
-__device__ __forceinline__ int vswz(int r, int c) {
-  if constexpr (NCH == 16) {
-    return c ^ (4 * (r & 3));
-  } else {
-    return c ^ (4 * ((r >> 1) & 1));
-  }
-}
+constexpr float TAU = 8.0f;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+template <bool V>
+struct Tag {
+  static constexpr bool value = V;
+};
+
+template <int D>
+struct Geo {
+  static constexpr int NCH = D / 8;                // 16-byte chunks per row
+  static constexpr int NDB = D / 32;               // 32-wide d blocks
+  static constexpr int NKS = D / 16;               // QK^T MFMA k-steps
+  // K: rows padded to NCH + 1 slots (16 bytes each): 16 consecutive rows at
+  // the same chunk land in 16 different 4-bank groups.
+  static constexpr int KSL = NCH + 1;
+  static constexpr int KSLOTS = BC * KSL;
+  static constexpr int KINS = KSLOTS / 64;         // 64-lane copies per block
+  static constexpr int KPW = (KINS + 3) / 4;       // per wave (at most)
+  // V: unpadded rows, 64-byte segments XOR-swizzled.
+  static constexpr int VSLOTS = BC * NCH;
+  static constexpr int VINS = VSLOTS / 64;
+  static constexpr int VPW = VINS / 4;
+  static_assert(KSLOTS % 64 == 0 && VSLOTS % 256 == 0, "copy tiling");
+};
+
+// Segment swizzle of V row r: the 4 rows read together by one transposing
+// read (r = 4a + R) must use 4 different 16-bank groups.
+template <int D>
+__device__ __forceinline__ int vx(int r) {
+  if constexpr (D == 128) {
+    return r & 3;
+  } else {
+    return (r >> 1) & 1;
+  }
+}
 
 // Transposing LDS read.  In each group of 16 lanes, lane 4R + j supplies the
 // address of 4 consecutive 16-bit elements; output lane i of the group gets
@@ -91,21 +112,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Lane l and lane l ^ 32 hold the two halves of the same query's row.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset bytes) into
+// LDS at `dst` + 16 * lane.  Offsets past the descriptor's size read zeros.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
+                                            const uint4* dst,
+                                            uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset, 0, 0,
+      0);
+}
+
+// Instruction-order groups for the scheduler.
+#define SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
+constexpr int SG_VALU = 0x002 | 0x400;   // VALU incl. transcendental
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DSR = 0x100;
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(NTHR, 2)
 fwd_bf16_kernel(const FwdArgs a) {
-  constexpr int NCH = D / 8;            // 16-byte chunks per K row
-  constexpr int NDB = D / 32;           // 32-row blocks of d (PV MFMA M-dim)
-  constexpr int NKS = D / 16;           // k-steps of the QK^T MFMA
-  constexpr int KROWS = NTHR / NCH;     // K rows loaded per pass
-  constexpr int KPASS = BC / KROWS;     // K loads per thread per tile
-
-  __shared__ uint4 Ks[2][BC * NCH];     // [key][d], swizzled
-  __shared__ uint4 Vs[2][BC * NCH];     // [key][d], swizzled
+  using G = Geo<D>;
+  __shared__ uint4 Ks0[G::KSLOTS];
+  __shared__ uint4 Ks1[G::KSLOTS];
+  __shared__ uint4 Vs0[G::VSLOTS];
+  __shared__ uint4 Vs1[G::VSLOTS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int li = lane & 31;             // MFMA column / row-in-block
   const int h = lane >> 5;              // lane half
 
@@ -128,66 +177,87 @@ fwd_bf16_kernel(const FwdArgs a) {
                        (static_cast<int64_t>(b) * a.Hkv + hk) * N * D;
 
   // ---- Q -> registers (B operand of S^T = K Q^T) ----
-  bf16x8_t qf[NKS];
+  bf16x8_t qf[G::NKS];
   {
     const uint32_t flip = a.neg ? 0x80008000u : 0u;
     const bool ok = qrow < N;
     const uint16_t* src = qp + static_cast<int64_t>(ok ? qrow : N - 1) * D +
                           h * (D / 2);
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const uint4 x = ldg16(src + 8 * s);
-      uint4 u = ok ? x : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < G::NKS; ++s) {
+      uint4 u = keep_if(ldg16(src + 8 * s), ok);
       u.x ^= flip; u.y ^= flip; u.z ^= flip; u.w ^= flip;
       qf[s] = as_bf16x8(u);
     }
   }
 
-  // ---- K/V tile staging (global -> registers -> LDS) ----
-  // Thread tid moves 16-byte chunk (tid % NCH) of rows tid / NCH + i * KROWS
-  // of both K and V: each group of NCH lanes reads one whole row.
-  uint4 kst[KPASS];
-  uint4 vst[KPASS];
-  const int kc = tid % NCH;
-  const int kr = tid / NCH;
-
-  auto load_tile = [&](int kv0) {
+  // ---- per-lane byte offsets of this wave's block copies ----
+  // K copy j (j = wave + 4 i) fills slots 64 j .. 64 j + 63: lane L writes
+  // slot 64 j + L = row * KSL + chunk; pad slots re-read the last chunk.
+  uint32_t koff[G::KPW];
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      // Rows past the end read row N-1 (always in bounds) and are zeroed.
-      const int r = kv0 + kr + i * KROWS;
-      const int64_t off = static_cast<int64_t>(min(r, N - 1)) * D + 8 * kc;
-      const uint4 kx = ldg16(kp + off);
-      const uint4 vx = ldg16(vp + off);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      kst[i] = (r < N) ? kx : z;
-      vst[i] = (r < N) ? vx : z;
-    }
+  for (int i = 0; i < G::KPW; ++i) {
+    const int slot = 64 * (wave + 4 * i) + lane;
+    const int row = slot / G::KSL;
+    const int ch = min(slot % G::KSL, G::NCH - 1);
+    koff[i] = static_cast<uint32_t>((row * D + ch * 8) * 2);
+  }
+  // V copy j: physical chunk p of row r holds logical chunk p with its
+  // segment bits XOR-ed by vx(r).
+  uint32_t voff[G::VPW];
+#pragma unroll
+  for (int i = 0; i < G::VPW; ++i) {
+    const int slot = 64 * (wave + 4 * i) + lane;
+    const int row = slot / G::NCH;
+    const int p = slot % G::NCH;
+    const int ch = (((p >> 2) ^ vx<D>(row)) << 2) | (p & 3);
+    voff[i] = static_cast<uint32_t>((row * D + ch * 8) * 2);
+  }
+  const int kinst = (G::KINS - wave + 3) / 4;   // copies this wave issues
+
+  // Descriptors of the K / V rows [kv0, N) of this (batch, KV head): copies
+  // of rows past N read zeros.
+  auto rsrc_at = [&](const uint16_t* base, int kv0) {
+    const int rows = max(N - kv0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + static_cast<int64_t>(kv0) * D), 0,
+        rows * D * 2, 0x00020000);
+  };
+  auto copy_k = [&](int t, const uint4* stage) {
+    const auto rs = rsrc_at(kp, t * BC);
+#pragma unroll
+    for (int i = 0; i < G::KPW; ++i)
+      if (i < kinst) copy_to_lds(rs, stage + 64 * (wave + 4 * i), koff[i]);
+  };
+  auto copy_v = [&](int t, const uint4* stage) {
+    const auto rs = rsrc_at(vp, t * BC);
+#pragma unroll
+    for (int i = 0; i < G::VPW; ++i)
+      copy_to_lds(rs, stage + 64 * (wave + 4 * i), voff[i]);
   };
 
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int r = kr + i * KROWS;
-      Ks[buf][r * NCH + swz<NCH>(r, kc)] = kst[i];
-      Vs[buf][r * NCH + vswz<NCH>(r, kc)] = vst[i];
-    }
-  };
-
-  // Per-lane part of the transposed V read (see lds_read_tr16): lane
-  // 16 g + 4 R + j reads key row R (+ the tile offsets) at d-chunk
-  // 2 (g % 2) + (j & 1) of a 32-wide d block, half (j >> 1).  The output
-  // lane then holds 4 keys of d = 32 db + sigma(lane % 32).
-  const int tr_g = lane >> 4;
+  // ---- per-lane LDS read offsets (bytes) ----
+  //   K (A operand of S^T): row sigma(li) + 32 kb, chunk h * NCH/2 + s.
+  const int rd_k = (sigma(li) * G::KSL + h * (G::NCH / 2)) * 16;
+  //   V (transposing read): lane 16 g + 4 R + j reads key row
+  //   32 kb + 16 u + 8 h + 4 t4 + R at d = 32 db + 16 (g % 2) + 8 (j & 1)
+  //   + 4 (j >> 1); the output lane then holds 4 keys of
+  //   d = 32 db + sigma(lane % 32).
   const int tr_R = (lane >> 2) & 3;
   const int tr_j = lane & 3;
-  const int tr_c = 2 * (tr_g & 1) + (tr_j & 1);       // + 4 db
-  const int tr_half = 4 * (tr_j >> 1);                  // 16-bit elements
+  int rd_v[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    const int r = 8 * h + tr_R;
+    const int seg = db ^ vx<D>(r);                   // 64-byte segment
+    const int ch = 4 * seg + 2 * ((lane >> 4) & 1) + (tr_j & 1);
+    rd_v[db] = (r * G::NCH + ch) * 16 + 8 * (tr_j >> 1);
+  }
 
   // ---- running softmax state (per lane = per query; both halves agree) ----
-  f32x16_t oacc[NDB];
+  f32x16_t oacc[G::NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16_t{};
+  for (int i = 0; i < G::NDB; ++i) oacc[i] = f32x16_t{};
   float m_run = -__builtin_inff();
   float l_run = 0.f;                    // this lane's half of the row sum
   const float c = a.c;
@@ -195,125 +265,196 @@ fwd_bf16_kernel(const FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kv0 = t * BC;
-    if (t + 1 < ntiles) load_tile(kv0 + BC);
-
-    const bool skip = CAUSAL && (kv0 > qw0 + 31);   // whole tile masked
-    if (!skip) {
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16_t sacc[2];
+  // S^T = K Q^T of one block from a K stage.
+  auto qk = [&](const uint4* ks, f32x16_t (&s_out)[2]) {
+    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(ks) + rd_k;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_out[kb] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < G::NKS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16_t{};
-        const int r = 32 * kb + sigma(li);
-        const uint4* row = &Ks[buf][r * NCH];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const uint4 kk = row[swz<NCH>(r, h * (NCH / 2) + s)];
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(kk), qf[s], sacc[kb], 0, 0, 0);
-        }
+        const uint4 kk = *reinterpret_cast<const uint4*>(
+            kb8 + 32 * kb * G::KSL * 16 + 16 * s);
+        s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kk), qf[s], s_out[kb], 0, 0, 0);
       }
+    }
+  };
 
-      // Mask: lane half h holds keys 32kb + 16(r/8) + 8h + (r%8).
-      const bool need_mask =
-          (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
-            const bool ok = key < N && (!CAUSAL || key <= qrow);
-            if (!ok) sacc[kb][r] = -__builtin_inff();
-          }
-        }
-      }
-
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-
-      float psum = 0.f;
-      bf16x8_t pb[2][2];
+  // Block statistics: mask (if needed: hidden scores become -inf), row max,
+  // and the lazy move of the running max with the rescale of O and l.
+  auto stats = [&](f32x16_t (&s)[2], int kv0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float s0 = sacc[kb][8 * u + 2 * e];
-            const float s1 = sacc[kb][8 * u + 2 * e + 1];
-            const float p0 = (s0 == -__builtin_inff())
-                                 ? 0.f
-                                 : __builtin_amdgcn_exp2f(fmaf(s0, c, -m_use));
-            const float p1 = (s1 == -__builtin_inff())
-                                 ? 0.f
-                                 : __builtin_amdgcn_exp2f(fmaf(s1, c, -m_use));
-            psum += p0 + p1;
-            w[e] = pack_bf16x2(p0, p1);
-          }
-          pb[kb][u] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // O^T += V^T P^T.  k-slot (h, e) of this 16-key step is key
-      // 32 kb + 16 u + 8 h + e on both operands.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r0 = 32 * kb + 16 * u + 8 * h + tr_R;   // key row, t4 = 0
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint16_t* v0 = reinterpret_cast<const uint16_t*>(
-                &Vs[buf][r0 * NCH + vswz<NCH>(r0, 4 * db + tr_c)]) + tr_half;
-            const uint16_t* v1 = reinterpret_cast<const uint16_t*>(
-                &Vs[buf][(r0 + 4) * NCH + vswz<NCH>(r0 + 4, 4 * db + tr_c)]) +
-                tr_half;
-            const i16x4_t lo = lds_read_tr16(v0);
-            const i16x4_t hi = lds_read_tr16(v1);
-            const bf16x8_t vv = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                vv, pb[kb][u], oacc[db], 0, 0, 0);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool ok = key < N && (!CAUSAL || key <= qrow);
+          if (!ok) s[kb][r] = -__builtin_inff();
         }
       }
     }
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    mx = half_max(mx);
+    float m_tile = mx * c;
+    if constexpr (MASKED) m_tile = (mx == -__builtin_inff()) ? mx : m_tile;
+    const bool grow = m_tile > m_run + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha =
+          grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  };
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+  // P = exp2(S c - m) as the bf16 B operand of P V, and the row sum.
+  // Masked scores are -inf and give p = 0 (c > 0 always: the launcher
+  // floors it at 1e-30, which leaves scale = 0 exact in fp32).
+  auto probs = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * u + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
+          const float p1 =
+              __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
+          w[e] = pack_bf16x2(p0, p1);
+          // fp32 sum of the unrounded p: the LSE needs it.
+          l_run += p0 + p1;
+        }
+        pb[kb][u] =
+            __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    }
+  };
+
+  // O^T += V^T P^T from a V stage.  k-slot (h, e) of each 16-key step is key
+  // 32 kb + 16 u + 8 h + e on both operands.
+  auto pv = [&](const uint4* vs, const bf16x8_t (&pb)[2][2]) {
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vs);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const uint8_t* p0 =
+              v8 + rd_v[db] + (32 * kb + 16 * u) * G::NCH * 16;
+          const i16x4_t lo = lds_read_tr16(p0);
+          const i16x4_t hi = lds_read_tr16(p0 + 4 * G::NCH * 16);
+          const bf16x8_t vv = __builtin_bit_cast(
+              bf16x8_t,
+              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              vv, pb[kb][u], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto masked_at = [&](int t) {
+    const int kv0 = t * BC;
+    return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+  };
+
+  auto wait_copies_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
     __syncthreads();
+  };
+
+  // One block t with S(t) in `s`: statistics, then [S(t+1) on the matrix
+  // core || P(t) on the vector unit], then O += P(t) V(t).  kr: K stage
+  // holding block t+1; vr: V stage holding block t; kw / vw: stages that
+  // receive blocks t+2 (K) and t+1 (V).
+  auto step = [&](int t, f32x16_t (&s)[2], const uint4* kr, const uint4* vr,
+                  const uint4* kw, const uint4* vw, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int kv0 = t * BC;
+    if (masked_at(t)) {
+      stats(s, kv0, Tag<true>{});
+    } else {
+      stats(s, kv0, Tag<false>{});
+    }
+    wait_copies_and_sync();
+    if constexpr (!LAST) {
+      if (t + 1 < ntiles) copy_v(t + 1, vw);
+      if (t + 2 < ntiles) copy_k(t + 2, kw);
+    }
+    bf16x8_t pb[2][2];
+    if constexpr (!LAST) {
+      f32x16_t sn[2];
+      qk(kr, sn);
+      probs(s, pb);
+      // MFMA (scores of t+1) interleaved with the exp / pack of block t.
+      SCHED_GROUP(SG_DSR, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * G::NKS; ++i) {
+        SCHED_GROUP(SG_MFMA, 1, 0);
+        SCHED_GROUP(SG_VALU, 7, 0);
+        if (i + 4 < 2 * G::NKS) SCHED_GROUP(SG_DSR, 1, 0);
+      }
+      pv(vr, pb);
+      SCHED_GROUP(SG_DSR, 6, 1);
+#pragma unroll
+      for (int i = 0; i < 4 * G::NDB; ++i) {
+        SCHED_GROUP(SG_MFMA, 1, 1);
+        if (2 * i + 6 < 8 * G::NDB) SCHED_GROUP(SG_DSR, 2, 1);
+      }
+      s[0] = sn[0];
+      s[1] = sn[1];
+    } else {
+      probs(s, pb);
+      pv(vr, pb);
+    }
+  };
+
+  // ---- prologue: blocks 0 (K, V) and 1 (K) into LDS, scores of block 0 ----
+  copy_k(0, Ks0);
+  copy_v(0, Vs0);
+  if (ntiles > 1) copy_k(1, Ks1);
+  wait_copies_and_sync();
+  f32x16_t s[2];
+  qk(Ks0, s);
+
+  // ---- main loop, unrolled by two so every stage is a fixed array ----
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<false>{});
+    step(t + 1, s, Ks0, Vs1, Ks1, Vs0, Tag<false>{});
+  }
+  if (t + 1 < ntiles) {
+    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<false>{});
+    step(t + 1, s, Ks0, Vs1, Ks1, Vs0, Tag<true>{});
+  } else {
+    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<true>{});
   }
 
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* op = static_cast<uint16_t*>(a.o) +
                    ((static_cast<int64_t>(b) * a.H + hq) * N + qrow) * D;
+    // Accumulator row m <-> d = 32 db + sigma(m): lane half h holds
+    // d = 32 db + 16 u + 8 h + (0..7) in registers 8 u .. 8 u + 7.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         uint4 w;
@@ -325,8 +466,9 @@ fwd_bf16_kernel(const FwdArgs a) {
       }
     }
     if (h == 0) {
+      const float m_fin = (m_run == -__builtin_inff()) ? 0.f : m_run;
       float* lp = a.lse + (static_cast<int64_t>(b) * a.H + hq) * N + qrow;
-      *lp = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * 0.69314718055994531f
+      *lp = (l_tot > 0.f) ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f
                           : -__builtin_inff();
     }
   }
@@ -345,6 +487,10 @@ hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
   a.nqb = (a.N + BR - 1) / BR;
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  // Per-(batch, KV head) byte ranges are addressed by 32-bit buffer
+  // offsets.
+  if (static_cast<long long>(a.N) * d * 2 > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
   if (d == 64) {

@@ -111,10 +111,8 @@ fwd_fp8_kernel(const FwdArgs a) {
         qp + static_cast<int64_t>(ok ? qrow : N - 1) * D + 64 * h);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint4 x0 = src[2 * s], x1 = src[2 * s + 1];
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      uint4 u0 = ok ? x0 : z;
-      uint4 u1 = ok ? x1 : z;
+      const uint4 u0 = keep_if(src[2 * s], ok);
+      const uint4 u1 = keep_if(src[2 * s + 1], ok);
       qf[s] = i32x8_t{(int)(u0.x ^ flip), (int)(u0.y ^ flip),
                       (int)(u0.z ^ flip), (int)(u0.w ^ flip),
                       (int)(u1.x ^ flip), (int)(u1.y ^ flip),
@@ -122,30 +120,30 @@ fwd_fp8_kernel(const FwdArgs a) {
     }
   }
 
-  uint4 kst[KPASS], vst[KPASS];
+  // Staging registers: thread tid moves 16-byte chunk (tid % NCH) of rows
+  // tid / NCH and tid / NCH + 32 of both K and V (KPASS == 2).
+  static_assert(KPASS == 2, "staging below is written for two passes");
+  uint4 k0s, k1s, v0s, v1s;
   const int kc = tid % NCH;
   const int kr = tid / NCH;
 
   auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      // Rows past the end read row N-1 (always in bounds) and are zeroed.
-      const int r = kv0 + kr + i * KROWS;
-      const int64_t off = static_cast<int64_t>(min(r, N - 1)) * D + 16 * kc;
-      const uint4 kx = *reinterpret_cast<const uint4*>(kp + off);
-      const uint4 vx = *reinterpret_cast<const uint4*>(vp + off);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      kst[i] = (r < N) ? kx : z;
-      vst[i] = (r < N) ? vx : z;
-    }
+    // Rows past the end read row N-1 (always in bounds).  Their scores are
+    // masked; their V values are zeroed so that P = 0 times V stays 0.
+    const int r0 = kv0 + kr, r1 = r0 + KROWS;
+    const int64_t o0 = static_cast<int64_t>(min(r0, N - 1)) * D + 16 * kc;
+    const int64_t o1 = static_cast<int64_t>(min(r1, N - 1)) * D + 16 * kc;
+    k0s = *reinterpret_cast<const uint4*>(kp + o0);
+    k1s = *reinterpret_cast<const uint4*>(kp + o1);
+    v0s = keep_if(*reinterpret_cast<const uint4*>(vp + o0), r0 < N);
+    v1s = keep_if(*reinterpret_cast<const uint4*>(vp + o1), r1 < N);
   };
   auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int r = kr + i * KROWS;
-      Ks[buf][r * NCH + kswz(r, kc)] = kst[i];
-      Vs[buf][r * NCH + vswz(r, kc)] = vst[i];
-    }
+    const int r0 = kr, r1 = kr + KROWS;
+    Ks[buf][r0 * NCH + kswz(r0, kc)] = k0s;
+    Ks[buf][r1 * NCH + kswz(r1, kc)] = k1s;
+    Vs[buf][r0 * NCH + vswz(r0, kc)] = v0s;
+    Vs[buf][r1 * NCH + vswz(r1, kc)] = v1s;
   };
 
   // Transposed V read, per lane: group g = lane / 16, lanes 2R + j of the
