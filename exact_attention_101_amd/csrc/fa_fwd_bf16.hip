@@ -265,45 +265,30 @@ fwd_bf16_kernel(const FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // S^T = K Q^T of one block from a K stage.
-  auto qk = [&](const uint4* ks, f32x16_t (&s_out)[2]) {
-    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(ks) + rd_k;
+  // Hide the scores of keys a row may not see (causal: key > query;
+  // ragged tail: key >= N) by setting them to -inf.  Lane half h holds keys
+  // kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
+  auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_out[kb] = f32x16_t{};
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int s = 0; s < G::NKS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(
-            kb8 + 32 * kb * G::KSL * 16 + 16 * s);
-        s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kk), qf[s], s_out[kb], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+        const bool ok = key < N && (!CAUSAL || key <= qrow);
+        if (!ok) s[kb][r] = -__builtin_inff();
       }
     }
   };
+  auto masked_at = [&](int t) {
+    const int kv0 = t * BC;
+    return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+  };
 
-  // Block statistics: mask (if needed: hidden scores become -inf), row max,
-  // and the lazy move of the running max with the rescale of O and l.
-  auto stats = [&](f32x16_t (&s)[2], int kv0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool ok = key < N && (!CAUSAL || key <= qrow);
-          if (!ok) s[kb][r] = -__builtin_inff();
-        }
-      }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
-    mx = half_max(mx);
+  // Lazy move of the running max from a block's (both-halves) raw max
+  // score mx, with the rescale of O and l when it moves (rare).
+  auto update_max = [&](float mx) {
     float m_tile = mx * c;
-    if constexpr (MASKED) m_tile = (mx == -__builtin_inff()) ? mx : m_tile;
+    m_tile = (mx == -__builtin_inff()) ? mx : m_tile;
     const bool grow = m_tile > m_run + TAU;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
       const float m_new = grow ? m_tile : m_run;
@@ -318,59 +303,118 @@ fwd_bf16_kernel(const FwdArgs a) {
     }
   };
 
-  // P = exp2(S c - m) as the bf16 B operand of P V, and the row sum.
-  // Masked scores are -inf and give p = 0 (c > 0 always: the launcher
-  // floors it at 1e-30, which leaves scale = 0 exact in fp32).
-  auto probs = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
+  // K fragment i of the scores product: k-step s = i / 2, key block
+  // kb = i % 2 (alternating the two accumulators).
+  auto kfrag = [&](const uint4* ks, int i) {
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(ks) + rd_k +
+                       32 * (i & 1) * G::KSL * 16 + 16 * (i >> 1);
+    return *reinterpret_cast<const uint4*>(p);
+  };
+  // Transposed V fragment j (two 8-byte reads) of P V step i = (kb, u, db).
+  auto vread = [&](const uint4* vs, int i, int half) {
+    const int db = i % G::NDB;
+    const int u = (i / G::NDB) & 1;
+    const int kb = i / (2 * G::NDB);
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(vs) + rd_v[db] +
+                       (32 * kb + 16 * u + 4 * half) * G::NCH * 16;
+    return lds_read_tr16(p);
+  };
+
+  constexpr int NQK = 2 * G::NKS;       // MFMAs of the scores product
+  constexpr int NPV = 4 * G::NDB;       // MFMAs of the P V product
+  constexpr int KPF = 4;                // K fragments read ahead
+  constexpr int VPF = 3;                // V steps read ahead
+
+  // Phase B: scores of the next block (kr) on the matrix core, interleaved
+  // slot by slot with P = exp2(S c - m) of the current block (fp32 row sum,
+  // bf16 pack).  Masked scores are -inf and give p = 0 (the launcher keeps
+  // c > 0).
+  auto phase_b = [&](const uint4* kr, const f32x16_t (&s)[2],
+                     f32x16_t (&sn)[2], bf16x8_t (&pb)[2][2], auto qk_tag) {
+    constexpr bool WITH_QK = decltype(qk_tag)::value;
     const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+    uint4 kf[KPF];
+    if constexpr (WITH_QK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * u + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-          const float p1 =
-              __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
-          w[e] = pack_bf16x2(p0, p1);
-          // fp32 sum of the unrounded p: the LSE needs it.
-          l_run += p0 + p1;
-        }
-        pb[kb][u] =
-            __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      }
+      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, i);
     }
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+    uint32_t w[16];
+    float ls0 = 0.f, ls1 = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if constexpr (WITH_QK) {
+        const uint4 kk = kf[i % KPF];
+        if (i + KPF < NQK) kf[i % KPF] = kfrag(kr, i + KPF);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kk), qf[i >> 1], sn[i & 1], 0, 0, 0);
+      }
+      // score pairs of this slot (16 pairs over NQK slots)
+#pragma unroll
+      for (int q = 0; q < 16 / NQK; ++q) {
+        const int pr = i * (16 / NQK) + q;          // pair 0..15
+        const int kb = pr >> 3, r = 2 * (pr & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
+        w[pr] = pack_bf16x2(p0, p1);
+        if (pr & 1) ls1 += p0 + p1; else ls0 += p0 + p1;
+        // Pin the work to this slot (otherwise it is sunk towards its use
+        // in the P V product, past the scheduling fences).
+        asm volatile("" : "+v"(w[pr]), "+v"(ls0), "+v"(ls1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += ls0 + ls1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pb[kb][u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
+                                 w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
   };
 
-  // O^T += V^T P^T from a V stage.  k-slot (h, e) of each 16-key step is key
-  // 32 kb + 16 u + 8 h + e on both operands.
-  auto pv = [&](const uint4* vs, const bf16x8_t (&pb)[2][2]) {
-    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vs);
+  // Phase C: O^T += V^T P^T from the V stage vr (k-slot (h, e) of each
+  // 16-key step is key 32 kb + 16 u + 8 h + e on both operands),
+  // interleaved with the raw row max of the next block's scores sn.
+  // Returns that max (both halves combined).
+  auto phase_c = [&](const uint4* vr, const bf16x8_t (&pb)[2][2],
+                     const f32x16_t (&sn)[2], bool with_max) {
+    i16x4_t vf[VPF][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int i = 0; i < VPF; ++i) {
+      vf[i][0] = vread(vr, i, 0);
+      vf[i][1] = vread(vr, i, 1);
+    }
+    float mx = -__builtin_inff();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+    for (int i = 0; i < NPV; ++i) {
+      const i16x4_t lo = vf[i % VPF][0], hi = vf[i % VPF][1];
+      if (i + VPF < NPV) {
+        vf[i % VPF][0] = vread(vr, i + VPF, 0);
+        vf[i % VPF][1] = vread(vr, i + VPF, 1);
+      }
+      const int db = i % G::NDB;
+      const int u = (i / G::NDB) & 1;
+      const int kb = i / (2 * G::NDB);
+      const bf16x8_t vv = __builtin_bit_cast(
+          bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u],
+                                                         oacc[db], 0, 0, 0);
+      if (with_max) {
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          const uint8_t* p0 =
-              v8 + rd_v[db] + (32 * kb + 16 * u) * G::NCH * 16;
-          const i16x4_t lo = lds_read_tr16(p0);
-          const i16x4_t hi = lds_read_tr16(p0 + 4 * G::NCH * 16);
-          const bf16x8_t vv = __builtin_bit_cast(
-              bf16x8_t,
-              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              vv, pb[kb][u], oacc[db], 0, 0, 0);
+        for (int q = 0; q < 32 / NPV; ++q) {
+          const int e = i * (32 / NPV) + q;
+          mx = fmaxf(mx, sn[e >> 4][e & 15]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-  auto masked_at = [&](int t) {
-    const int kv0 = t * BC;
-    return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+    return with_max ? half_max(mx) : mx;
   };
 
   auto wait_copies_and_sync = [&]() {
@@ -378,49 +422,29 @@ fwd_bf16_kernel(const FwdArgs a) {
     __syncthreads();
   };
 
-  // One block t with S(t) in `s`: statistics, then [S(t+1) on the matrix
-  // core || P(t) on the vector unit], then O += P(t) V(t).  kr: K stage
-  // holding block t+1; vr: V stage holding block t; kw / vw: stages that
-  // receive blocks t+2 (K) and t+1 (V).
+  // One block t whose scores are in `s` (masked, max applied): [scores of
+  // t+1 || P(t)], then [O += P(t) V(t) || max of t+1], then the lazy max
+  // update for t+1.  kr: K stage holding block t+1; vr: V stage holding
+  // block t; kw / vw: stages receiving blocks t+2 (K) and t+1 (V).
   auto step = [&](int t, f32x16_t (&s)[2], const uint4* kr, const uint4* vr,
                   const uint4* kw, const uint4* vw, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int kv0 = t * BC;
-    if (masked_at(t)) {
-      stats(s, kv0, Tag<true>{});
-    } else {
-      stats(s, kv0, Tag<false>{});
-    }
     wait_copies_and_sync();
+    bf16x8_t pb[2][2];
     if constexpr (!LAST) {
       if (t + 1 < ntiles) copy_v(t + 1, vw);
       if (t + 2 < ntiles) copy_k(t + 2, kw);
-    }
-    bf16x8_t pb[2][2];
-    if constexpr (!LAST) {
       f32x16_t sn[2];
-      qk(kr, sn);
-      probs(s, pb);
-      // MFMA (scores of t+1) interleaved with the exp / pack of block t.
-      SCHED_GROUP(SG_DSR, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * G::NKS; ++i) {
-        SCHED_GROUP(SG_MFMA, 1, 0);
-        SCHED_GROUP(SG_VALU, 7, 0);
-        if (i + 4 < 2 * G::NKS) SCHED_GROUP(SG_DSR, 1, 0);
-      }
-      pv(vr, pb);
-      SCHED_GROUP(SG_DSR, 6, 1);
-#pragma unroll
-      for (int i = 0; i < 4 * G::NDB; ++i) {
-        SCHED_GROUP(SG_MFMA, 1, 1);
-        if (2 * i + 6 < 8 * G::NDB) SCHED_GROUP(SG_DSR, 2, 1);
-      }
+      phase_b(kr, s, sn, pb, Tag<true>{});
+      if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BC);
+      const float mx = phase_c(vr, pb, sn, true);
+      update_max(mx);
       s[0] = sn[0];
       s[1] = sn[1];
     } else {
-      probs(s, pb);
-      pv(vr, pb);
+      f32x16_t sn[2];
+      phase_b(kr, s, sn, pb, Tag<false>{});
+      phase_c(vr, pb, sn, false);
     }
   };
 
@@ -430,7 +454,19 @@ fwd_bf16_kernel(const FwdArgs a) {
   if (ntiles > 1) copy_k(1, Ks1);
   wait_copies_and_sync();
   f32x16_t s[2];
-  qk(Ks0, s);
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
+#pragma unroll
+  for (int i = 0; i < NQK; ++i)
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(kfrag(Ks0, i)), qf[i >> 1], s[i & 1], 0, 0, 0);
+  if (masked_at(0)) apply_mask(s, 0);
+  {
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    update_max(half_max(mx));
+  }
 
   // ---- main loop, unrolled by two so every stage is a fixed array ----
   int t = 0;
