@@ -207,6 +207,21 @@ def main() -> int:
         extras["fp8_quantize_hadamard_per_tensor"] = {
             "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xq, xk, xv, q8, k8, v8, oo, ll
+        # Context, not part of the path: the vendor bf16 GEMM (hipBLASLt via
+        # torch.matmul) on N(0,1) operands of the same distribution, i.e. what
+        # a tuned library contraction reaches on this card under its power
+        # limit.
+        g = torch.Generator(device=dev).manual_seed(7)
+        a = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
+        bt = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
+        c = torch.empty((8192, 8192), device=dev, dtype=torch.bfloat16)
+        mg = _time_launches(lambda: torch.matmul(a, bt, out=c), 20, 5)
+        tg = 2 * 8192 ** 3 / (mg * 1e-3) / 1e12
+        extras["library_gemm_bf16_8192_randn"] = {
+            "ms": round(mg, 4), "TFLOP/s": round(tg, 1),
+            "frac_of_bf16_peak": round(tg / BF16_PEAK_TFLOPS, 4)}
+        del a, bt, c
 
     cpu = None
     if not args.no_cpu and rank == 0:
