@@ -37,10 +37,15 @@
 //     computes the scores of block t+1, the vector unit turns the scores of
 //     block t into P; then the P V product of block t runs.  The order is
 //     pinned with scheduling-group barriers;
-//   * the running maximum is only moved when a block's maximum exceeds it by
-//     more than TAU (log2 units).  Any reference value gives the same
-//     softmax (the shift cancels between numerator and denominator), so this
-//     stays exact; it bounds p by 2^TAU and makes the rescale of O rare;
+//   * the running maximum m is a reference value, not necessarily the exact
+//     maximum: any m gives the same softmax (the shift cancels between
+//     numerator and denominator), so P is first formed with the m already
+//     held.  Only if a lane's sum of the block's p exceeds 2^TAU (some score
+//     rose more than TAU log2 units above m; also inf / NaN, which is how the
+//     first block, with m = -inf, is caught) does the wave take the exact
+//     step: row maximum of the block, move m, rescale O and l, form P
+//     again.  All p stay in [0, 2^TAU], and the common path computes no row
+//     maximum at all;
 //   * LDS layouts are chosen so every MFMA operand read is free of bank
 //     conflicts: K rows are padded by one 16-byte slot, V rows XOR their
 //     64-byte segments with the key's position in its group of 4.
@@ -53,7 +58,7 @@ namespace {
 constexpr int BR = 128;
 constexpr int BC = 64;
 constexpr int NTHR = 256;
-constexpr float TAU = 8.0f;
+constexpr float TAU_EXP2 = 256.0f;   // 2^TAU, TAU = 8 (log2 units)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
@@ -284,23 +289,45 @@ fwd_bf16_kernel(const FwdArgs a) {
     return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
   };
 
-  // Lazy move of the running max from a block's (both-halves) raw max
-  // score mx, with the rescale of O and l when it moves (rare).
-  auto update_max = [&](float mx) {
-    float m_tile = mx * c;
-    m_tile = (mx == -__builtin_inff()) ? mx : m_tile;
-    const bool grow = m_tile > m_run + TAU;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha =
-          grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = m_new;
-      l_run *= alpha;
+  // Exact step for a block whose scores s gave a lane sum above 2^TAU (or
+  // inf / NaN): move m to the block's row maximum if that is larger, rescale
+  // O and l, and form P again.  Returns the new lane sum of the block.
+  auto exact_block = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
+    float mx = s[0][0];
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db)
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    mx = half_max(mx);
+    const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = (m_new == -__builtin_inff())
+                            ? 1.0f
+                            : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    // A row with no visible key so far keeps m = -inf; its p are all 0.
+    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    uint32_t w[16];
+    float ls = 0.f;
+#pragma unroll
+    for (int pr = 0; pr < 16; ++pr) {
+      const int kb = pr >> 3, r = 2 * (pr & 7);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
+      w[pr] = pack_bf16x2(p0, p1);
+      ls += p0 + p1;
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pb[kb][u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
+                                 w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
+    return ls;
   };
 
   // K fragment i of the scores product: k-step s = i / 2, key block
@@ -326,13 +353,14 @@ fwd_bf16_kernel(const FwdArgs a) {
   constexpr int VPF = 3;                // V steps read ahead
 
   // Phase B: scores of the next block (kr) on the matrix core, interleaved
-  // slot by slot with P = exp2(S c - m) of the current block (fp32 row sum,
+  // slot by slot with P = exp2(S c - m) of the current block (fp32 lane sum,
   // bf16 pack).  Masked scores are -inf and give p = 0 (the launcher keeps
-  // c > 0).
+  // c > 0).  With m = -inf every p is inf or NaN, which the sum test after
+  // this phase sends to the exact step.  Returns the lane sum.
   auto phase_b = [&](const uint4* kr, const f32x16_t (&s)[2],
                      f32x16_t (&sn)[2], bf16x8_t (&pb)[2][2], auto qk_tag) {
     constexpr bool WITH_QK = decltype(qk_tag)::value;
-    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+    const float m_use = m_run;
     uint4 kf[KPF];
     if constexpr (WITH_QK) {
 #pragma unroll
@@ -367,7 +395,6 @@ fwd_bf16_kernel(const FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += ls0 + ls1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -375,21 +402,25 @@ fwd_bf16_kernel(const FwdArgs a) {
         pb[kb][u] = __builtin_bit_cast(
             bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
                                  w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
+    return ls0 + ls1;
+  };
+
+  // Accept the block's P (lane sum ls) or redo it exactly, then add it to l.
+  auto settle = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2], float ls) {
+    const bool bad = !(ls <= TAU_EXP2);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_block(s, pb);
+    l_run += ls;
   };
 
   // Phase C: O^T += V^T P^T from the V stage vr (k-slot (h, e) of each
-  // 16-key step is key 32 kb + 16 u + 8 h + e on both operands),
-  // interleaved with the raw row max of the next block's scores sn.
-  // Returns that max (both halves combined).
-  auto phase_c = [&](const uint4* vr, const bf16x8_t (&pb)[2][2],
-                     const f32x16_t (&sn)[2], bool with_max) {
+  // 16-key step is key 32 kb + 16 u + 8 h + e on both operands).
+  auto phase_c = [&](const uint4* vr, const bf16x8_t (&pb)[2][2]) {
     i16x4_t vf[VPF][2];
 #pragma unroll
     for (int i = 0; i < VPF; ++i) {
       vf[i][0] = vread(vr, i, 0);
       vf[i][1] = vread(vr, i, 1);
     }
-    float mx = -__builtin_inff();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -405,16 +436,8 @@ fwd_bf16_kernel(const FwdArgs a) {
           bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u],
                                                          oacc[db], 0, 0, 0);
-      if (with_max) {
-#pragma unroll
-        for (int q = 0; q < 32 / NPV; ++q) {
-          const int e = i * (32 / NPV) + q;
-          mx = fmaxf(mx, sn[e >> 4][e & 15]);
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return with_max ? half_max(mx) : mx;
   };
 
   auto wait_copies_and_sync = [&]() {
@@ -422,10 +445,10 @@ fwd_bf16_kernel(const FwdArgs a) {
     __syncthreads();
   };
 
-  // One block t whose scores are in `s` (masked, max applied): [scores of
-  // t+1 || P(t)], then [O += P(t) V(t) || max of t+1], then the lazy max
-  // update for t+1.  kr: K stage holding block t+1; vr: V stage holding
-  // block t; kw / vw: stages receiving blocks t+2 (K) and t+1 (V).
+  // One block t whose scores are in `s` (masked): [scores of t+1 || P(t)],
+  // the sum test of P(t), then O += P(t) V(t).  kr: K stage holding block
+  // t+1; vr: V stage holding block t; kw / vw: stages receiving blocks t+2
+  // (K) and t+1 (V).
   auto step = [&](int t, f32x16_t (&s)[2], const uint4* kr, const uint4* vr,
                   const uint4* kw, const uint4* vw, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
@@ -435,16 +458,17 @@ fwd_bf16_kernel(const FwdArgs a) {
       if (t + 1 < ntiles) copy_v(t + 1, vw);
       if (t + 2 < ntiles) copy_k(t + 2, kw);
       f32x16_t sn[2];
-      phase_b(kr, s, sn, pb, Tag<true>{});
+      const float ls = phase_b(kr, s, sn, pb, Tag<true>{});
+      settle(s, pb, ls);
       if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BC);
-      const float mx = phase_c(vr, pb, sn, true);
-      update_max(mx);
+      phase_c(vr, pb);
       s[0] = sn[0];
       s[1] = sn[1];
     } else {
       f32x16_t sn[2];
-      phase_b(kr, s, sn, pb, Tag<false>{});
-      phase_c(vr, pb, sn, false);
+      const float ls = phase_b(kr, s, sn, pb, Tag<false>{});
+      settle(s, pb, ls);
+      phase_c(vr, pb);
     }
   };
 
@@ -461,12 +485,6 @@ fwd_bf16_kernel(const FwdArgs a) {
     s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         as_bf16x8(kfrag(Ks0, i)), qf[i >> 1], s[i & 1], 0, 0, 0);
   if (masked_at(0)) apply_mask(s, 0);
-  {
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
-    update_max(half_max(mx));
-  }
 
   // ---- main loop, unrolled by two so every stage is a fixed array ----
   int t = 0;
