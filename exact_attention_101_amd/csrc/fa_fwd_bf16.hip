@@ -132,14 +132,16 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset bytes) into
-// LDS at `dst` + 16 * lane.  Offsets past the descriptor's size read zeros.
+// One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset + soffset
+// bytes; soffset is wave-uniform) into LDS at `dst` + 16 * lane.  Offsets
+// past the descriptor's size read zeros.
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
                                             const uint4* dst,
-                                            uint32_t voffset) {
+                                            uint32_t voffset,
+                                            uint32_t soffset = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset, 0, 0,
-      0);
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset,
+      soffset, 0, 0);
 }
 
 // Instruction-order groups for the scheduler.
@@ -199,25 +201,38 @@ fwd_bf16_kernel(const FwdArgs a) {
   // ---- per-lane byte offsets of this wave's block copies ----
   // K copy j (j = wave + 4 i) fills slots 64 j .. 64 j + 63: lane L writes
   // slot 64 j + L = row * KSL + chunk; pad slots re-read the last chunk.
-  uint32_t koff[G::KPW];
-#pragma unroll
-  for (int i = 0; i < G::KPW; ++i) {
+  // Offsets are below 2^15: copies 2 i2 and 2 i2 + 1 share a register, and
+  // a copy past the first four (the last window, one wave) computes its
+  // offsets when issued.
+  auto k_offset = [&](int i) {
     const int slot = 64 * (wave + 4 * i) + lane;
     const int row = slot / G::KSL;
-    const int ch = min(slot % G::KSL, G::NCH - 1);
-    koff[i] = static_cast<uint32_t>((row * D + ch * 8) * 2);
-  }
-  // V copy j: physical chunk p of row r holds logical chunk p with its
-  // segment bits XOR-ed by vx(r).
-  uint32_t voff[G::VPW];
+    const int ch = min(slot - row * G::KSL, G::NCH - 1);
+    return static_cast<uint32_t>((row * D + ch * 8) * 2);
+  };
+  constexpr int KREG = G::KPW < 4 ? G::KPW : 4;   // copies with a register
+  constexpr int KPK = (KREG + 1) / 2;
+  uint32_t koff2[KPK];
 #pragma unroll
-  for (int i = 0; i < G::VPW; ++i) {
-    const int slot = 64 * (wave + 4 * i) + lane;
+  for (int i2 = 0; i2 < KPK; ++i2) {
+    uint32_t pk = k_offset(2 * i2);
+    if (2 * i2 + 1 < KREG) pk |= k_offset(2 * i2 + 1) << 16;
+    koff2[i2] = pk;
+  }
+  static_assert(BC * D * 2 <= 0x8000, "K copy offsets fit in 15 bits");
+  // V copy j (j = wave + 4 i): physical chunk p of row r holds logical chunk
+  // p with its segment bits XOR-ed by vx(r).  Copy i covers the rows of copy
+  // 0 plus 256 / NCH * i, whose vx is the same, so its offsets are those of
+  // copy 0 plus 4096 i bytes (a wave-uniform soffset).
+  uint32_t voff0;
+  {
+    const int slot = 64 * wave + lane;
     const int row = slot / G::NCH;
     const int p = slot % G::NCH;
     const int ch = (((p >> 2) ^ vx<D>(row)) << 2) | (p & 3);
-    voff[i] = static_cast<uint32_t>((row * D + ch * 8) * 2);
+    voff0 = static_cast<uint32_t>((row * D + ch * 8) * 2);
   }
+  static_assert((256 / G::NCH) * D * 2 == 4096, "V copy stride");
   const int kinst = (G::KINS - wave + 3) / 4;   // copies this wave issues
 
   // Descriptors of the K / V rows [kv0, N) of this (batch, KV head): copies
@@ -232,13 +247,16 @@ fwd_bf16_kernel(const FwdArgs a) {
     const auto rs = rsrc_at(kp, t * BC);
 #pragma unroll
     for (int i = 0; i < G::KPW; ++i)
-      if (i < kinst) copy_to_lds(rs, stage + 64 * (wave + 4 * i), koff[i]);
+      if (i < kinst)
+        copy_to_lds(rs, stage + 64 * (wave + 4 * i),
+                    i < KREG ? (koff2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu
+                             : k_offset(i));
   };
   auto copy_v = [&](int t, const uint4* stage) {
     const auto rs = rsrc_at(vp, t * BC);
 #pragma unroll
     for (int i = 0; i < G::VPW; ++i)
-      copy_to_lds(rs, stage + 64 * (wave + 4 * i), voff[i]);
+      copy_to_lds(rs, stage + 64 * (wave + 4 * i), voff0, 4096u * i);
   };
 
   // ---- per-lane LDS read offsets (bytes) ----
@@ -250,13 +268,14 @@ fwd_bf16_kernel(const FwdArgs a) {
   //   d = 32 db + sigma(lane % 32).
   const int tr_R = (lane >> 2) & 3;
   const int tr_j = lane & 3;
-  int rd_v[G::NDB];
-#pragma unroll
-  for (int db = 0; db < G::NDB; ++db) {
+  //   The 64-byte segment index sits in address bits 6-7 (bit 6 for D = 64)
+  //   and is the only part that depends on db: rd_v0 ^ (db << 6).
+  int rd_v0;
+  {
     const int r = 8 * h + tr_R;
-    const int seg = db ^ vx<D>(r);                   // 64-byte segment
+    const int seg = vx<D>(r);                        // segment of db = 0
     const int ch = 4 * seg + 2 * ((lane >> 4) & 1) + (tr_j & 1);
-    rd_v[db] = (r * G::NCH + ch) * 16 + 8 * (tr_j >> 1);
+    rd_v0 = (r * G::NCH + ch) * 16 + 8 * (tr_j >> 1);
   }
 
   // ---- running softmax state (per lane = per query; both halves agree) ----
@@ -289,13 +308,14 @@ fwd_bf16_kernel(const FwdArgs a) {
     return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
   };
 
-  // Exact step for a block whose scores s gave a lane sum above 2^TAU (or
-  // inf / NaN): move m to the block's row maximum if that is larger, rescale
-  // O and l, and form P again.  Returns the new lane sum of the block.
-  auto exact_block = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
-    float mx = s[0][0];
+  // Exact step for a block whose P (formed with the held m) has a lane sum
+  // above 2^TAU, or inf / NaN: from the block's scores sx, move m to the
+  // row maximum if that is larger, rescale O and l, and form P again in w.
+  // Returns the new lane sum of the block.
+  auto exact_block = [&](const f32x16_t (&sx)[2], uint32_t (&w)[16]) {
+    float mx = sx[0][0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sx[i >> 4][i & 15]);
     mx = half_max(mx);
     const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
     const float m_new = fmaxf(m_run, m_tile);
@@ -310,26 +330,17 @@ fwd_bf16_kernel(const FwdArgs a) {
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     // A row with no visible key so far keeps m = -inf; its p are all 0.
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    uint32_t w[16];
     float ls = 0.f;
 #pragma unroll
     for (int pr = 0; pr < 16; ++pr) {
       const int kb = pr >> 3, r = 2 * (pr & 7);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[kb][r], c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[kb][r + 1], c, -m_use));
       w[pr] = pack_bf16x2(p0, p1);
       ls += p0 + p1;
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        pb[kb][u] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
-                                 w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
     return ls;
   };
-
   // K fragment i of the scores product: k-step s = i / 2, key block
   // kb = i % 2 (alternating the two accumulators).
   auto kfrag = [&](const uint4* ks, int i) {
@@ -342,59 +353,20 @@ fwd_bf16_kernel(const FwdArgs a) {
     const int db = i % G::NDB;
     const int u = (i / G::NDB) & 1;
     const int kb = i / (2 * G::NDB);
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(vs) + rd_v[db] +
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(vs) + (rd_v0 ^ (db << 6)) +
                        (32 * kb + 16 * u + 4 * half) * G::NCH * 16;
     return lds_read_tr16(p);
   };
 
   constexpr int NQK = 2 * G::NKS;       // MFMAs of the scores product
   constexpr int NPV = 4 * G::NDB;       // MFMAs of the P V product
-  constexpr int KPF = 4;                // K fragments read ahead
-  constexpr int VPF = 3;                // V steps read ahead
+  static_assert(NQK == NPV, "one scores MFMA per P V MFMA");
+  constexpr int NSL = NQK;              // issue slots per step
+  constexpr int PPS = 16 / NSL;         // score pairs turned into P per slot
+  constexpr int KPF = 2;                // K fragments read ahead
+  constexpr int VPF = 2;                // V steps read ahead
 
-  // Phase B: scores of the next block (kr) on the matrix core, interleaved
-  // slot by slot with P = exp2(S c - m) of the current block (fp32 lane sum,
-  // bf16 pack).  Masked scores are -inf and give p = 0 (the launcher keeps
-  // c > 0).  With m = -inf every p is inf or NaN, which the sum test after
-  // this phase sends to the exact step.  Returns the lane sum.
-  auto phase_b = [&](const uint4* kr, const f32x16_t (&s)[2],
-                     f32x16_t (&sn)[2], bf16x8_t (&pb)[2][2], auto qk_tag) {
-    constexpr bool WITH_QK = decltype(qk_tag)::value;
-    const float m_use = m_run;
-    uint4 kf[KPF];
-    if constexpr (WITH_QK) {
-#pragma unroll
-      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, i);
-    }
-    sn[0] = f32x16_t{};
-    sn[1] = f32x16_t{};
-    uint32_t w[16];
-    float ls0 = 0.f, ls1 = 0.f;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      if constexpr (WITH_QK) {
-        const uint4 kk = kf[i % KPF];
-        if (i + KPF < NQK) kf[i % KPF] = kfrag(kr, i + KPF);
-        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kk), qf[i >> 1], sn[i & 1], 0, 0, 0);
-      }
-      // score pairs of this slot (16 pairs over NQK slots)
-#pragma unroll
-      for (int q = 0; q < 16 / NQK; ++q) {
-        const int pr = i * (16 / NQK) + q;          // pair 0..15
-        const int kb = pr >> 3, r = 2 * (pr & 7);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
-        w[pr] = pack_bf16x2(p0, p1);
-        if (pr & 1) ls1 += p0 + p1; else ls0 += p0 + p1;
-        // Pin the work to this slot (otherwise it is sunk towards its use
-        // in the P V product, past the scheduling fences).
-        asm volatile("" : "+v"(w[pr]), "+v"(ls0), "+v"(ls1));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  auto pack_p = [&](const uint32_t (&w)[16], bf16x8_t (&pb)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -402,26 +374,121 @@ fwd_bf16_kernel(const FwdArgs a) {
         pb[kb][u] = __builtin_bit_cast(
             bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
                                  w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
-    return ls0 + ls1;
   };
 
-  // Accept the block's P (lane sum ls) or redo it exactly, then add it to l.
-  auto settle = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2], float ls) {
+  // Accept P of block t (scores s, P packed in w, lane sum ls) or take the
+  // exact step first, then add the block to l.
+  auto settle = [&](const f32x16_t (&s)[2], uint32_t (&w)[16], float ls) {
     const bool bad = !(ls <= TAU_EXP2);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_block(s, pb);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_block(s, w);  // rare
     l_run += ls;
   };
 
-  // Phase C: O^T += V^T P^T from the V stage vr (k-slot (h, e) of each
-  // 16-key step is key 32 kb + 16 u + 8 h + e on both operands).
-  auto phase_c = [&](const uint4* vr, const bf16x8_t (&pb)[2][2]) {
+  auto wait_copies_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
+    __syncthreads();
+  };
+
+  // Step t of the three-stage pipeline.  On entry `s` holds the (masked)
+  // scores of block t and `pp` the settled P of block t-1; the K stage kr
+  // holds block t+1 and the V stage vr block t-1.  Every issue slot pairs
+  // one MFMA of the scores of block t+1 (QK) and one MFMA of
+  // O += P(t-1) V(t-1) (PV) with PPS score pairs of block t turned into P
+  // (p = exp2(S c - m), fp32 lane sum, bf16 pack), so the vector unit works
+  // while the matrix core runs.  Masked scores are -inf and give p = 0 (the
+  // launcher keeps c > 0); with m = -inf every p is inf or NaN, which the
+  // sum test sends to the exact step.  The step first waits for the copies
+  // of the previous step and then starts those of V(t) into vw and K(t+2)
+  // into kw.
+  auto step = [&](int t, f32x16_t (&s)[2], bf16x8_t (&pp)[2][2],
+                  const uint4* kr, const uint4* vr, const uint4* kw,
+                  const uint4* vw, auto qk_tag, auto pv_tag) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    wait_copies_and_sync();
+    copy_v(t, vw);
+    if (t + 2 < ntiles) copy_k(t + 2, kw);
+    const float m_use = m_run;
+    uint4 kf[KPF];
+    i16x4_t vf[VPF][2];
+    if constexpr (QK) {
+#pragma unroll
+      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, i);
+    }
+    if constexpr (PV) {
+#pragma unroll
+      for (int i = 0; i < VPF; ++i) {
+        vf[i][0] = vread(vr, i, 0);
+        vf[i][1] = vread(vr, i, 1);
+      }
+    }
+    f32x16_t sn[2];
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+    uint32_t w[16];
+    float ls0 = 0.f, ls1 = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      if constexpr (QK) {
+        const uint4 kk = kf[i % KPF];
+        if (i + KPF < NQK) kf[i % KPF] = kfrag(kr, i + KPF);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kk), qf[i >> 1], sn[i & 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < PPS; ++q) {
+        const int pr = i * PPS + q;                 // pair 0..15
+        const int kb = pr >> 3, r = 2 * (pr & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
+        w[pr] = pack_bf16x2(p0, p1);
+        if (pr & 1) ls1 += p0 + p1; else ls0 += p0 + p1;
+        // Pin the work to this slot (otherwise it is sunk towards its use
+        // in the next step, past the scheduling fences).
+        asm volatile("" : "+v"(w[pr]), "+v"(ls0), "+v"(ls1));
+      }
+      if constexpr (PV) {
+        const i16x4_t lo = vf[i % VPF][0], hi = vf[i % VPF][1];
+        if (i + VPF < NPV) {
+          vf[i % VPF][0] = vread(vr, i + VPF, 0);
+          vf[i % VPF][1] = vread(vr, i + VPF, 1);
+        }
+        const int db = i % G::NDB;
+        const int u = (i / G::NDB) & 1;
+        const int kb = i / (2 * G::NDB);
+        const bf16x8_t vv = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pp[kb][u],
+                                                           oacc[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    settle(s, w, ls0 + ls1);
+    bf16x8_t pb[2][2];
+    pack_p(w, pb);
+    if constexpr (QK) {
+      if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BC);
+      s[0] = sn[0];
+      s[1] = sn[1];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pp[kb][u] = pb[kb][u];
+  };
+
+  // Last product: O += P(T-1) V(T-1) from the V stage vr (k-slot (h, e) of
+  // each 16-key step is key 32 kb + 16 u + 8 h + e on both operands).
+  auto final_pv = [&](const uint4* vr, const bf16x8_t (&pp)[2][2]) {
+    wait_copies_and_sync();
     i16x4_t vf[VPF][2];
 #pragma unroll
     for (int i = 0; i < VPF; ++i) {
       vf[i][0] = vread(vr, i, 0);
       vf[i][1] = vread(vr, i, 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const i16x4_t lo = vf[i % VPF][0], hi = vf[i % VPF][1];
@@ -434,47 +501,16 @@ fwd_bf16_kernel(const FwdArgs a) {
       const int kb = i / (2 * G::NDB);
       const bf16x8_t vv = __builtin_bit_cast(
           bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u],
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pp[kb][u],
                                                          oacc[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  auto wait_copies_and_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
-    __syncthreads();
-  };
-
-  // One block t whose scores are in `s` (masked): [scores of t+1 || P(t)],
-  // the sum test of P(t), then O += P(t) V(t).  kr: K stage holding block
-  // t+1; vr: V stage holding block t; kw / vw: stages receiving blocks t+2
-  // (K) and t+1 (V).
-  auto step = [&](int t, f32x16_t (&s)[2], const uint4* kr, const uint4* vr,
-                  const uint4* kw, const uint4* vw, auto last_tag) {
-    constexpr bool LAST = decltype(last_tag)::value;
-    wait_copies_and_sync();
-    bf16x8_t pb[2][2];
-    if constexpr (!LAST) {
-      if (t + 1 < ntiles) copy_v(t + 1, vw);
-      if (t + 2 < ntiles) copy_k(t + 2, kw);
-      f32x16_t sn[2];
-      const float ls = phase_b(kr, s, sn, pb, Tag<true>{});
-      settle(s, pb, ls);
-      if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BC);
-      phase_c(vr, pb);
-      s[0] = sn[0];
-      s[1] = sn[1];
-    } else {
-      f32x16_t sn[2];
-      const float ls = phase_b(kr, s, sn, pb, Tag<false>{});
-      settle(s, pb, ls);
-      phase_c(vr, pb);
-    }
-  };
-
-  // ---- prologue: blocks 0 (K, V) and 1 (K) into LDS, scores of block 0 ----
+  // ---- prologue: K blocks 0 and 1 into LDS, scores of block 0 ----
+  // Stages by parity of the step t: step t reads K(t+1) from Ks[(t+1) % 2]
+  // and V(t-1) from Vs[(t-1) % 2] and fills Ks[t % 2] with K(t+2) and
+  // Vs[t % 2] with V(t).
   copy_k(0, Ks0);
-  copy_v(0, Vs0);
   if (ntiles > 1) copy_k(1, Ks1);
   wait_copies_and_sync();
   f32x16_t s[2];
@@ -485,18 +521,39 @@ fwd_bf16_kernel(const FwdArgs a) {
     s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         as_bf16x8(kfrag(Ks0, i)), qf[i >> 1], s[i & 1], 0, 0, 0);
   if (masked_at(0)) apply_mask(s, 0);
-
-  // ---- main loop, unrolled by two so every stage is a fixed array ----
-  int t = 0;
-  for (; t + 2 < ntiles; t += 2) {
-    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<false>{});
-    step(t + 1, s, Ks0, Vs1, Ks1, Vs0, Tag<false>{});
+  {
+    // Reference max from block 0 (every row sees key 0, so m is finite).
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    mx = half_max(mx);
+    m_run = (mx == -__builtin_inff()) ? mx : mx * c;
   }
-  if (t + 1 < ntiles) {
-    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<false>{});
-    step(t + 1, s, Ks0, Vs1, Ks1, Vs0, Tag<true>{});
+  bf16x8_t pp[2][2];
+
+  // ---- steps 0 .. T-1, then the last product ----
+  const int last = ntiles - 1;
+  if (last == 0) {
+    step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{}, Tag<false>{});
+    final_pv(Vs0, pp);
   } else {
-    step(t, s, Ks1, Vs0, Ks0, Vs1, Tag<true>{});
+    step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{}, Tag<false>{});
+    int t = 1;
+    for (; t + 2 <= last; t += 2) {            // steps t (odd), t + 1 (even)
+      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{}, Tag<true>{});
+      step(t + 1, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{}, Tag<true>{});
+    }
+    if (t < last) {                           // one more odd step
+      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{}, Tag<true>{});
+      ++t;
+    }
+    if (t & 1) {                              // t == last
+      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<false>{}, Tag<true>{});
+      final_pv(Vs1, pp);
+    } else {
+      step(t, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{}, Tag<true>{});
+      final_pv(Vs0, pp);
+    }
   }
 
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
