@@ -15,18 +15,29 @@ LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = [
+# Code generation flags shared by the library build and the ISA checks.
+CODEGEN = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
+    # Keep the compiler from forming packed fp32 VALU ops.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMAs the compiler emits write vector registers (the attention scores
+    # are read by VALU code); accumulators meant for AGPRs are pinned there
+    # explicitly in the kernels.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+]
+FLAGS = [
+    *CODEGEN,
     "-fPIC",
     "-shared",
     "-fvisibility=hidden",
-    # Keep the compiler from forming packed fp32 VALU ops.
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
+# gfx950 assembly of one source (device code only), for inspection and tests.
+FLAGS_DEVICE_ASM = [*CODEGEN, "--cuda-device-only", "-S",
+                    "-Wno-unused-command-line-argument"]
 
 
 def build(verbose: bool = False) -> str:

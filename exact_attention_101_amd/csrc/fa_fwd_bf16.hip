@@ -13,15 +13,21 @@
 // производительность с FlashAttention-4".
 //
 // gfx950 mapping:
-//   * workgroup = 4 waves, BR = 128 query rows (32 per wave), K/V blocks of
-//     BC = 64 keys.  K and V blocks go from HBM/L2 straight into LDS with
-//     buffer_load_dwordx4 ... lds (no register staging), into four distinct
-//     LDS stage arrays (two for K, two for V) so the compiler can tell the
-//     in-flight copies from the stages being read;
+//   * workgroup = 4 waves, one per SIMD; each wave owns 64 query rows as two
+//     32-row MFMA blocks, so BR = 256.  Every K or V fragment a wave reads
+//     from LDS feeds two MFMAs (one per query block): LDS reads per FLOP
+//     are half of what 32-row waves need, and LDS traffic is what the
+//     matrix cores otherwise wait on and what the power budget goes to;
+//   * K and V blocks of BT = 64 keys go from HBM/L2 straight into LDS with
+//     buffer_load_dwordx4 ... lds (no register staging), into two K and two
+//     V stage arrays (distinct arrays, so the compiler can tell the
+//     in-flight copies from the stages being read).  Compute steps take
+//     BC = 32 keys, so copies and the workgroup barrier come every second
+//     step;
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: the accumulator column is the query, so each
-//     lane holds 32 scores of one query and the row max / row sum are
-//     in-lane plus one v_permlane32_swap between the two lane halves;
+//     lane holds the 16 scores of one query per 32-key step, and a row's
+//     two halves sit in lanes l and l ^ 32;
 //   * Q lives in registers as the B operand for the whole kernel; the
 //     contraction over d is permuted so that lane half h holds the
 //     contiguous d-range [h*D/2, (h+1)*D/2);
@@ -31,21 +37,21 @@
 //     (V^T) is read with the transposing ds_read_b64_tr_b16;
 //   * softmax in fp32 registers in the log2 domain: p = exp2(S*c - m) with
 //     c = |scale| * log2(e) (one FMA + v_exp_f32 per score), fp32 row sums;
-//   * the two matrix products overlap the softmax inside each wave (the
-//     intra-group overlap of the FlashAttention-3 summary, section
-//     «Assincronia: sobreposição de GEMM e Softmax»): while the matrix core
-//     computes the scores of block t+1, the vector unit turns the scores of
-//     block t into P; then the P V product of block t runs.  The order is
-//     pinned with scheduling-group barriers;
+//   * a three-stage software pipeline overlaps the two matrix products with
+//     the softmax inside each wave (the intra-group overlap of the
+//     FlashAttention-3 summary, section «Assincronia: sobreposição de GEMM e
+//     Softmax»): step b issues, slot by slot, one MFMA of the scores of
+//     block b+1, one MFMA of O += P(b-1) V(b-1) and one pair of
+//     p = exp2(S c - m) of block b, so the vector unit works while the
+//     matrix core runs.  The order is pinned with scheduling barriers;
 //   * the running maximum m is a reference value, not necessarily the exact
 //     maximum: any m gives the same softmax (the shift cancels between
 //     numerator and denominator), so P is first formed with the m already
 //     held.  Only if a lane's sum of the block's p exceeds 2^TAU (some score
-//     rose more than TAU log2 units above m; also inf / NaN, which is how the
-//     first block, with m = -inf, is caught) does the wave take the exact
-//     step: row maximum of the block, move m, rescale O and l, form P
-//     again.  All p stay in [0, 2^TAU], and the common path computes no row
-//     maximum at all;
+//     rose more than TAU = 8 log2 units above m; also inf / NaN) does the
+//     wave take the exact step: row maximum of the block, move m, rescale O
+//     and l, form P again.  All p stay in [0, 2^TAU]; block 0 sets m from
+//     its exact row maximum, so the common path computes no maximum at all;
 //   * LDS layouts are chosen so every MFMA operand read is free of bank
 //     conflicts: K rows are padded by one 16-byte slot, V rows XOR their
 //     64-byte segments with the key's position in its group of 4.
@@ -55,16 +61,23 @@ namespace fa {
 
 namespace {
 
-constexpr int BR = 128;
-constexpr int BC = 64;
-constexpr int NTHR = 256;
-constexpr float TAU_EXP2 = 256.0f;   // 2^TAU, TAU = 8 (log2 units)
+constexpr int NWAVE = 4;
+constexpr int QPW = 64;                 // query rows per wave
+constexpr int BR = NWAVE * QPW;         // query rows per workgroup
+constexpr int BT = 64;                  // keys per K / V stage (copy tile)
+constexpr int BC = 32;                  // keys per compute step
+constexpr int NTHR = 64 * NWAVE;
+constexpr float TAU_EXP2 = 256.0f;      // 2^TAU, TAU = 8 (log2 units)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 template <bool V>
 struct Tag {
   static constexpr bool value = V;
+};
+template <int V>
+struct Int {
+  static constexpr int value = V;
 };
 
 template <int D>
@@ -75,14 +88,15 @@ struct Geo {
   // K: rows padded to NCH + 1 slots (16 bytes each): 16 consecutive rows at
   // the same chunk land in 16 different 4-bank groups.
   static constexpr int KSL = NCH + 1;
-  static constexpr int KSLOTS = BC * KSL;
-  static constexpr int KINS = KSLOTS / 64;         // 64-lane copies per block
-  static constexpr int KPW = (KINS + 3) / 4;       // per wave (at most)
+  static constexpr int KSLOTS = BT * KSL;
+  static constexpr int KINS = KSLOTS / 64;         // 64-lane copies per tile
+  static constexpr int KPW = (KINS + NWAVE - 1) / NWAVE;   // per wave, max
   // V: unpadded rows, 64-byte segments XOR-swizzled.
-  static constexpr int VSLOTS = BC * NCH;
+  static constexpr int VSLOTS = BT * NCH;
   static constexpr int VINS = VSLOTS / 64;
-  static constexpr int VPW = VINS / 4;
-  static_assert(KSLOTS % 64 == 0 && VSLOTS % 256 == 0, "copy tiling");
+  static constexpr int VPW = VINS / NWAVE;
+  static_assert(KSLOTS % 64 == 0 && VSLOTS % (64 * NWAVE) == 0,
+                "copy tiling");
 };
 
 // Segment swizzle of V row r: the 4 rows read together by one transposing
@@ -132,6 +146,35 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// O^T += V^T P^T with the accumulator held in accumulation registers (the
+// 128 fp32 values of O per lane for D = 128 do not fit in the vector
+// registers next to Q, S and P).  The library is built with VGPR-form
+// MFMAs for the compiler's own MFMA instructions (the scores, which the
+// vector unit reads); this one is written out so that its accumulator stays
+// in AGPRs without being moved around.  The compiler does not see that the
+// statement is an MFMA, so every other access of O is fenced by hand: reads
+// after acc_read_fence(), writes followed by acc_write_fence().  The ISA
+// test in the test suite checks the compiled kernels for accesses of an
+// accumulator within the MFMA's latency.
+__device__ __forceinline__ void mfma_pv_acc(const bf16x8_t& a,
+                                            const bf16x8_t& b,
+                                            f32x16_t& acc) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc)
+               : "v"(a), "v"(b));
+}
+// Wait states between the last mfma_pv_acc and any other access of its
+// accumulator: an 8-pass MFMA result needs 11 before a VALU or memory
+// instruction may read or overwrite it; 3 x s_nop 7 give 24.
+__device__ __forceinline__ void acc_read_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+// Wait states between a VALU write of an accumulator and the next
+// mfma_pv_acc reading it as its C operand.
+__device__ __forceinline__ void acc_write_fence() {
+  asm volatile("s_nop 4" ::: "memory");
+}
+
 // One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset + soffset
 // bytes; soffset is wave-uniform) into LDS at `dst` + 16 * lane.  Offsets
 // past the descriptor's size read zeros.
@@ -144,14 +187,8 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
       soffset, 0, 0);
 }
 
-// Instruction-order groups for the scheduler.
-#define SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
-constexpr int SG_VALU = 0x002 | 0x400;   // VALU incl. transcendental
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DSR = 0x100;
-
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NTHR, 2)
+__global__ void __launch_bounds__(NTHR, 1)
 fwd_bf16_kernel(const FwdArgs a) {
   using G = Geo<D>;
   __shared__ uint4 Ks0[G::KSLOTS];
@@ -165,16 +202,16 @@ fwd_bf16_kernel(const FwdArgs a) {
   const int li = lane & 31;             // MFMA column / row-in-block
   const int h = lane >> 5;              // lane half
 
-  int bh, qb;
+  int bh, qblk;
   map_work(blockIdx.x, gridDim.x, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh,
-           qb);
+           qblk);
   const int b = bh / a.H;
   const int hq = bh % a.H;
   const int hk = hq / a.group;
   const int N = a.N;
-  const int q0 = qb * BR;
-  const int qw0 = q0 + wave * 32;       // first query row of this wave
-  const int qrow = qw0 + li;            // this lane's query row
+  const int q0 = qblk * BR;
+  const int qw0 = q0 + wave * QPW;      // first query row of this wave
+  // This lane's query rows: qw0 + 32 j + li for query block j = 0, 1.
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                        (static_cast<int64_t>(b) * a.H + hq) * N * D;
@@ -183,29 +220,37 @@ fwd_bf16_kernel(const FwdArgs a) {
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) +
                        (static_cast<int64_t>(b) * a.Hkv + hk) * N * D;
 
-  // ---- Q -> registers (B operand of S^T = K Q^T) ----
-  bf16x8_t qf[G::NKS];
+  // ---- Q -> registers (B operand of S^T = K Q^T), two query blocks ----
+  bf16x8_t qf[2][G::NKS];
   {
     const uint32_t flip = a.neg ? 0x80008000u : 0u;
-    const bool ok = qrow < N;
-    const uint16_t* src = qp + static_cast<int64_t>(ok ? qrow : N - 1) * D +
-                          h * (D / 2);
 #pragma unroll
-    for (int s = 0; s < G::NKS; ++s) {
-      uint4 u = keep_if(ldg16(src + 8 * s), ok);
-      u.x ^= flip; u.y ^= flip; u.z ^= flip; u.w ^= flip;
-      qf[s] = as_bf16x8(u);
+    for (int j = 0; j < 2; ++j) {
+      const int row = qw0 + 32 * j + li;
+      const bool ok = row < N;
+      const uint16_t* src = qp + static_cast<int64_t>(ok ? row : N - 1) * D +
+                            h * (D / 2);
+#pragma unroll
+      for (int s = 0; s < G::NKS; ++s) {
+        uint4 u = keep_if(ldg16(src + 8 * s), ok);
+        u.x ^= flip; u.y ^= flip; u.z ^= flip; u.w ^= flip;
+        qf[j][s] = as_bf16x8(u);
+        // Q is only ever an MFMA operand, which MFMA reads from
+        // accumulation registers directly: keep it there and leave the
+        // vector registers to the scores and probabilities.
+        asm volatile("" : "+a"(qf[j][s]));
+      }
     }
   }
 
-  // ---- per-lane byte offsets of this wave's block copies ----
+  // ---- per-lane byte offsets of this wave's tile copies ----
   // K copy j (j = wave + 4 i) fills slots 64 j .. 64 j + 63: lane L writes
   // slot 64 j + L = row * KSL + chunk; pad slots re-read the last chunk.
   // Offsets are below 2^15: copies 2 i2 and 2 i2 + 1 share a register, and
   // a copy past the first four (the last window, one wave) computes its
   // offsets when issued.
   auto k_offset = [&](int i) {
-    const int slot = 64 * (wave + 4 * i) + lane;
+    const int slot = 64 * (wave + NWAVE * i) + lane;
     const int row = slot / G::KSL;
     const int ch = min(slot - row * G::KSL, G::NCH - 1);
     return static_cast<uint32_t>((row * D + ch * 8) * 2);
@@ -219,7 +264,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     if (2 * i2 + 1 < KREG) pk |= k_offset(2 * i2 + 1) << 16;
     koff2[i2] = pk;
   }
-  static_assert(BC * D * 2 <= 0x8000, "K copy offsets fit in 15 bits");
+  static_assert(BT * D * 2 <= 0x8000, "K copy offsets fit in 15 bits");
   // V copy j (j = wave + 4 i): physical chunk p of row r holds logical chunk
   // p with its segment bits XOR-ed by vx(r).  Copy i covers the rows of copy
   // 0 plus 256 / NCH * i, whose vx is the same, so its offsets are those of
@@ -232,44 +277,54 @@ fwd_bf16_kernel(const FwdArgs a) {
     const int ch = (((p >> 2) ^ vx<D>(row)) << 2) | (p & 3);
     voff0 = static_cast<uint32_t>((row * D + ch * 8) * 2);
   }
-  static_assert((256 / G::NCH) * D * 2 == 4096, "V copy stride");
-  const int kinst = (G::KINS - wave + 3) / 4;   // copies this wave issues
+  static_assert((64 * NWAVE / G::NCH) * D * 2 == 4096, "V copy stride");
+  const int kinst = (G::KINS - wave + NWAVE - 1) / NWAVE;   // K copies issued
 
-  // Descriptors of the K / V rows [kv0, N) of this (batch, KV head): copies
-  // of rows past N read zeros.
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
+  const int ntiles = (kv_end + BT - 1) / BT;
+  const int nblk = 2 * ntiles;          // key blocks of BC keys
+  // Steps 1 .. nsteps run in rounds of four; step b ends with O += P(b-1)
+  // V(b-1), so the last real block is done at step nblk.  Blocks past the
+  // real ones are virtual: their copies read zeros (the buffer descriptors
+  // end at kv_end) and their scores are masked, so their p are 0.
+  const int nsteps = (nblk + 3) & ~3;
+
+  // Descriptors of the K / V rows [kv0, kv_end) of this (batch, KV head):
+  // copies of rows past the last key this workgroup needs read zeros.
   auto rsrc_at = [&](const uint16_t* base, int kv0) {
-    const int rows = max(N - kv0, 0);
+    const int rows = max(kv_end - kv0, 0);
     return __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(base + static_cast<int64_t>(kv0) * D), 0,
         rows * D * 2, 0x00020000);
   };
-  auto copy_k = [&](int t, const uint4* stage) {
-    const auto rs = rsrc_at(kp, t * BC);
+  auto copy_k = [&](int tile, const uint4* stage) {
+    const auto rs = rsrc_at(kp, tile * BT);
 #pragma unroll
     for (int i = 0; i < G::KPW; ++i)
       if (i < kinst)
-        copy_to_lds(rs, stage + 64 * (wave + 4 * i),
+        copy_to_lds(rs, stage + 64 * (wave + NWAVE * i),
                     i < KREG ? (koff2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu
                              : k_offset(i));
   };
-  auto copy_v = [&](int t, const uint4* stage) {
-    const auto rs = rsrc_at(vp, t * BC);
+  auto copy_v = [&](int tile, const uint4* stage) {
+    const auto rs = rsrc_at(vp, tile * BT);
 #pragma unroll
     for (int i = 0; i < G::VPW; ++i)
-      copy_to_lds(rs, stage + 64 * (wave + 4 * i), voff0, 4096u * i);
+      copy_to_lds(rs, stage + 64 * (wave + NWAVE * i), voff0, 4096u * i);
   };
 
   // ---- per-lane LDS read offsets (bytes) ----
-  //   K (A operand of S^T): row sigma(li) + 32 kb, chunk h * NCH/2 + s.
+  //   K (A operand of S^T): row sigma(li) of the 32-key half kh of a stage,
+  //   chunk h * NCH/2 + s.
   const int rd_k = (sigma(li) * G::KSL + h * (G::NCH / 2)) * 16;
   //   V (transposing read): lane 16 g + 4 R + j reads key row
-  //   32 kb + 16 u + 8 h + 4 t4 + R at d = 32 db + 16 (g % 2) + 8 (j & 1)
+  //   32 kh + 16 u + 8 h + 4 t4 + R at d = 32 db + 16 (g % 2) + 8 (j & 1)
   //   + 4 (j >> 1); the output lane then holds 4 keys of
-  //   d = 32 db + sigma(lane % 32).
+  //   d = 32 db + sigma(lane % 32).  The 64-byte segment index sits in
+  //   address bits 6-7 (bit 6 for D = 64) and is the only part that depends
+  //   on db: rd_v0 ^ (db << 6).
   const int tr_R = (lane >> 2) & 3;
   const int tr_j = lane & 3;
-  //   The 64-byte segment index sits in address bits 6-7 (bit 6 for D = 64)
-  //   and is the only part that depends on db: rd_v0 ^ (db << 6).
   int rd_v0;
   {
     const int r = 8 * h + tr_R;
@@ -278,240 +333,258 @@ fwd_bf16_kernel(const FwdArgs a) {
     rd_v0 = (r * G::NCH + ch) * 16 + 8 * (tr_j >> 1);
   }
 
-  // ---- running softmax state (per lane = per query; both halves agree) ----
-  f32x16_t oacc[G::NDB];
+  // ---- running softmax state (per lane and query block; halves agree) ----
+  f32x16_t oacc[2][G::NDB];
 #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;                    // this lane's half of the row sum
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < G::NDB; ++i) oacc[j][i] = f32x16_t{};
+  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l_run[2] = {0.f, 0.f};          // this lane's half of the row sums
   const float c = a.c;
-
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
 
   // Hide the scores of keys a row may not see (causal: key > query;
   // ragged tail: key >= N) by setting them to -inf.  Lane half h holds keys
-  // kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
+  // kv0 + 16 (r / 8) + 8 h + (r % 8) of the 32-key block.
   auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int j = 0; j < 2; ++j) {
+      const int qrow = qw0 + 32 * j + li;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+        const int key = kv0 + 16 * (r >> 3) + 8 * h + (r & 7);
         const bool ok = key < N && (!CAUSAL || key <= qrow);
-        if (!ok) s[kb][r] = -__builtin_inff();
+        if (!ok) s[j][r] = -__builtin_inff();
       }
     }
   };
-  auto masked_at = [&](int t) {
-    const int kv0 = t * BC;
+  auto masked_at = [&](int blk) {
+    const int kv0 = blk * BC;
     return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
   };
 
   // Exact step for a block whose P (formed with the held m) has a lane sum
-  // above 2^TAU, or inf / NaN: from the block's scores sx, move m to the
-  // row maximum if that is larger, rescale O and l, and form P again in w.
-  // Returns the new lane sum of the block.
-  auto exact_block = [&](const f32x16_t (&sx)[2], uint32_t (&w)[16]) {
-    float mx = sx[0][0];
+  // above 2^TAU, or inf / NaN: from the block's scores s, move each query
+  // block's m to its row maximum if that is larger, rescale O and l, and
+  // form P again in w.  Returns the new lane sums in ls.
+  auto exact_block = [&](const f32x16_t (&s)[2], uint32_t (&w)[16],
+                         float (&ls)[2]) {
+    acc_read_fence();
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sx[i >> 4][i & 15]);
-    mx = half_max(mx);
-    const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-    const float m_new = fmaxf(m_run, m_tile);
-    const float alpha = (m_new == -__builtin_inff())
-                            ? 1.0f
-                            : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    for (int j = 0; j < 2; ++j) {
+      float mx = s[j][0];
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+      mx = half_max(mx);
+      const float m_blk = (mx == -__builtin_inff()) ? mx : mx * c;
+      const float m_new = fmaxf(m_run[j], m_blk);
+      const float alpha = (m_new == -__builtin_inff())
+                              ? 1.0f
+                              : __builtin_amdgcn_exp2f(m_run[j] - m_new);
+      m_run[j] = m_new;
+      l_run[j] *= alpha;
+      // One accumulator at a time (16 vector registers of temporaries).
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    // A row with no visible key so far keeps m = -inf; its p are all 0.
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    float ls = 0.f;
+      for (int db = 0; db < G::NDB; ++db) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int pr = 0; pr < 16; ++pr) {
-      const int kb = pr >> 3, r = 2 * (pr & 7);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[kb][r], c, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[kb][r + 1], c, -m_use));
-      w[pr] = pack_bf16x2(p0, p1);
-      ls += p0 + p1;
+        for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // A row with no visible key so far keeps m = -inf; its p are all 0.
+      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[j][2 * q], c, -m_use));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[j][2 * q + 1], c, -m_use));
+        w[8 * j + q] = pack_bf16x2(p0, p1);
+        sum += p0 + p1;
+      }
+      ls[j] = sum;
     }
-    return ls;
+    acc_write_fence();
   };
-  // K fragment i of the scores product: k-step s = i / 2, key block
-  // kb = i % 2 (alternating the two accumulators).
-  auto kfrag = [&](const uint4* ks, int i) {
+
+  // K fragment s (k-step over d) of the 32-key half kh of stage ks.
+  auto kfrag = [&](const uint4* ks, int kh, int s) {
     const uint8_t* p = reinterpret_cast<const uint8_t*>(ks) + rd_k +
-                       32 * (i & 1) * G::KSL * 16 + 16 * (i >> 1);
+                       32 * kh * G::KSL * 16 + 16 * s;
     return *reinterpret_cast<const uint4*>(p);
   };
-  // Transposed V fragment j (two 8-byte reads) of P V step i = (kb, u, db).
-  auto vread = [&](const uint4* vs, int i, int half) {
-    const int db = i % G::NDB;
-    const int u = (i / G::NDB) & 1;
-    const int kb = i / (2 * G::NDB);
-    const uint8_t* p = reinterpret_cast<const uint8_t*>(vs) + (rd_v0 ^ (db << 6)) +
-                       (32 * kb + 16 * u + 4 * half) * G::NCH * 16;
+  // Transposed V fragment f = (db, u) (two 8-byte reads, hf = 0, 1) of the
+  // 32-key half kh of stage vs: d block db, 16-key step u.
+  auto vread = [&](const uint4* vs, int kh, int f, int hf) {
+    const int db = f % G::NDB;
+    const int u = f / G::NDB;
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(vs) +
+                       (rd_v0 ^ (db << 6)) +
+                       (32 * kh + 16 * u + 4 * hf) * G::NCH * 16;
     return lds_read_tr16(p);
   };
 
-  constexpr int NQK = 2 * G::NKS;       // MFMAs of the scores product
-  constexpr int NPV = 4 * G::NDB;       // MFMAs of the P V product
+  constexpr int NQK = 2 * G::NKS;       // scores MFMAs per step (2 blocks)
+  constexpr int NPV = 4 * G::NDB;       // P V MFMAs per step (2 blocks)
   static_assert(NQK == NPV, "one scores MFMA per P V MFMA");
   constexpr int NSL = NQK;              // issue slots per step
   constexpr int PPS = 16 / NSL;         // score pairs turned into P per slot
   constexpr int KPF = 2;                // K fragments read ahead
-  constexpr int VPF = 2;                // V steps read ahead
-
-  auto pack_p = [&](const uint32_t (&w)[16], bf16x8_t (&pb)[2][2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        pb[kb][u] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(w[8 * kb + 4 * u], w[8 * kb + 4 * u + 1],
-                                 w[8 * kb + 4 * u + 2], w[8 * kb + 4 * u + 3]));
-  };
-
-  // Accept P of block t (scores s, P packed in w, lane sum ls) or take the
-  // exact step first, then add the block to l.
-  auto settle = [&](const f32x16_t (&s)[2], uint32_t (&w)[16], float ls) {
-    const bool bad = !(ls <= TAU_EXP2);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_block(s, w);  // rare
-    l_run += ls;
-  };
+  constexpr int VPF = 2;                // V fragments read ahead
+  constexpr int NVF = 2 * G::NDB;       // V fragments per step
 
   auto wait_copies_and_sync = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
     __syncthreads();
   };
 
-  // Step t of the three-stage pipeline.  On entry `s` holds the (masked)
-  // scores of block t and `pp` the settled P of block t-1; the K stage kr
-  // holds block t+1 and the V stage vr block t-1.  Every issue slot pairs
-  // one MFMA of the scores of block t+1 (QK) and one MFMA of
-  // O += P(t-1) V(t-1) (PV) with PPS score pairs of block t turned into P
-  // (p = exp2(S c - m), fp32 lane sum, bf16 pack), so the vector unit works
-  // while the matrix core runs.  Masked scores are -inf and give p = 0 (the
-  // launcher keeps c > 0); with m = -inf every p is inf or NaN, which the
-  // sum test sends to the exact step.  The step first waits for the copies
-  // of the previous step and then starts those of V(t) into vw and K(t+2)
-  // into kw.
-  auto step = [&](int t, f32x16_t (&s)[2], bf16x8_t (&pp)[2][2],
+  auto mfma_pv = [&](const i16x4_t (&vv)[2], const bf16x8_t& pb,
+                     f32x16_t& acc) {
+    const bf16x8_t v8 = __builtin_bit_cast(
+        bf16x8_t,
+        __builtin_shufflevector(vv[0], vv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    mfma_pv_acc(v8, pb, acc);
+  };
+
+  // Step blk of the three-stage pipeline.  On entry `s` holds the (masked)
+  // scores of block blk and `pp` the settled P of block blk-1.  The K stage
+  // kr (32-key half KH) holds block blk+1, the V stage vr (half VH) block
+  // blk-1.  Every issue slot pairs one MFMA of the scores of block blk+1
+  // (QK) and one MFMA of O += P(blk-1) V(blk-1) (PV) with PPS score pairs
+  // of block blk turned into P (p = exp2(S c - m), fp32 lane sums, bf16
+  // pack).  Masked scores are -inf and give p = 0 (the launcher keeps
+  // c > 0).  A SYNC step (odd blk) first waits for the copies issued two
+  // steps earlier, then starts those of tiles (blk-1)/2 + 2 (K, into kw)
+  // and (blk-1)/2 + 1 (V, into vw).
+  auto step = [&](int blk, f32x16_t (&s)[2], bf16x8_t (&pp)[2][2],
                   const uint4* kr, const uint4* vr, const uint4* kw,
-                  const uint4* vw, auto qk_tag, auto pv_tag) {
-    constexpr bool QK = decltype(qk_tag)::value;
+                  const uint4* vw, auto kh_tag, auto vh_tag, auto sync_tag,
+                  auto pv_tag) {
+    constexpr int KH = decltype(kh_tag)::value;
+    constexpr int VH = decltype(vh_tag)::value;
+    constexpr bool SYNC = decltype(sync_tag)::value;
+    constexpr bool QK = true;
     constexpr bool PV = decltype(pv_tag)::value;
-    wait_copies_and_sync();
-    copy_v(t, vw);
-    if (t + 2 < ntiles) copy_k(t + 2, kw);
-    const float m_use = m_run;
+    if constexpr (SYNC) {
+      wait_copies_and_sync();
+      const int tile = (blk - 1) >> 1;
+      copy_v(tile + 1, vw);
+      copy_k(tile + 2, kw);
+    }
+    const float mu0 = m_run[0], mu1 = m_run[1];
     uint4 kf[KPF];
     i16x4_t vf[VPF][2];
     if constexpr (QK) {
 #pragma unroll
-      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, i);
+      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, KH, i);
     }
     if constexpr (PV) {
 #pragma unroll
       for (int i = 0; i < VPF; ++i) {
-        vf[i][0] = vread(vr, i, 0);
-        vf[i][1] = vread(vr, i, 1);
+        vf[i][0] = vread(vr, VH, i, 0);
+        vf[i][1] = vread(vr, VH, i, 1);
       }
     }
     f32x16_t sn[2];
     sn[0] = f32x16_t{};
     sn[1] = f32x16_t{};
     uint32_t w[16];
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls00 = 0.f, ls01 = 0.f, ls10 = 0.f, ls11 = 0.f;
+    uint4 kcur = {};
+    i16x4_t vcur[2] = {};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
+      // Each slot: scores MFMA, then p = exp2(S c - m) for PPS pairs while
+      // it runs; P V MFMA, then the bf16 packs and lane sums of those pairs
+      // while that one runs.  With one wave per SIMD, this keeps vector work
+      // under both MFMAs and puts the exp latency between the two halves.
       if constexpr (QK) {
-        const uint4 kk = kf[i % KPF];
-        if (i + KPF < NQK) kf[i % KPF] = kfrag(kr, i + KPF);
+        // k-step i / 2 for query block i % 2: the fragment serves both.
+        if ((i & 1) == 0) {
+          const int f = i >> 1;
+          kcur = kf[f % KPF];
+          if (f + KPF < G::NKS) kf[f % KPF] = kfrag(kr, KH, f + KPF);
+        }
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kk), qf[i >> 1], sn[i & 1], 0, 0, 0);
+            as_bf16x8(kcur), qf[i & 1][i >> 1], sn[i & 1], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      float e[PPS][2];
 #pragma unroll
       for (int q = 0; q < PPS; ++q) {
         const int pr = i * PPS + q;                 // pair 0..15
-        const int kb = pr >> 3, r = 2 * (pr & 7);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
-        w[pr] = pack_bf16x2(p0, p1);
-        if (pr & 1) ls1 += p0 + p1; else ls0 += p0 + p1;
-        // Pin the work to this slot (otherwise it is sunk towards its use
-        // in the next step, past the scheduling fences).
-        asm volatile("" : "+v"(w[pr]), "+v"(ls0), "+v"(ls1));
+        const int j = pr >> 3, r = 2 * (pr & 7);    // query block, register
+        const float mu = j ? mu1 : mu0;
+        e[q][0] = __builtin_amdgcn_exp2f(fmaf(s[j][r], c, -mu));
+        e[q][1] = __builtin_amdgcn_exp2f(fmaf(s[j][r + 1], c, -mu));
+        // Pin the work to this slot (otherwise it is sunk towards its use,
+        // past the scheduling fences).
+        asm volatile("" : "+v"(e[q][0]), "+v"(e[q][1]));
       }
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (PV) {
-        const i16x4_t lo = vf[i % VPF][0], hi = vf[i % VPF][1];
-        if (i + VPF < NPV) {
-          vf[i % VPF][0] = vread(vr, i + VPF, 0);
-          vf[i % VPF][1] = vread(vr, i + VPF, 1);
+        // V fragment i / 2 = (db, u) for query block i % 2.
+        const int f = i >> 1;
+        if ((i & 1) == 0) {
+          vcur[0] = vf[f % VPF][0];
+          vcur[1] = vf[f % VPF][1];
+          if (f + VPF < NVF) {
+            vf[f % VPF][0] = vread(vr, VH, f + VPF, 0);
+            vf[f % VPF][1] = vread(vr, VH, f + VPF, 1);
+          }
         }
-        const int db = i % G::NDB;
-        const int u = (i / G::NDB) & 1;
-        const int kb = i / (2 * G::NDB);
-        const bf16x8_t vv = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pp[kb][u],
-                                                           oacc[db], 0, 0, 0);
+        mfma_pv(vcur, pp[i & 1][f / G::NDB], oacc[i & 1][f % G::NDB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < PPS; ++q) {
+        const int pr = i * PPS + q;
+        const int j = pr >> 3;
+        const float p0 = e[q][0], p1 = e[q][1];
+        w[pr] = pack_bf16x2(p0, p1);
+        if (j == 0) {
+          if (pr & 1) ls01 += p0 + p1; else ls00 += p0 + p1;
+        } else {
+          if (pr & 1) ls11 += p0 + p1; else ls10 += p0 + p1;
+        }
+        asm volatile("" : "+v"(w[pr]), "+v"(ls00), "+v"(ls01), "+v"(ls10),
+                     "+v"(ls11));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    settle(s, w, ls0 + ls1);
-    bf16x8_t pb[2][2];
-    pack_p(w, pb);
+    // Accept P of block blk or take the exact step first, then add it to l.
+    float ls[2] = {ls00 + ls01, ls10 + ls11};
+    const bool bad = !(ls[0] <= TAU_EXP2) || !(ls[1] <= TAU_EXP2);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) exact_block(s, w, ls);  // rare
+    l_run[0] += ls[0];
+    l_run[1] += ls[1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pp[j][u] = __builtin_bit_cast(
+            bf16x8_t,
+            make_uint4(w[8 * j + 4 * u], w[8 * j + 4 * u + 1],
+                       w[8 * j + 4 * u + 2], w[8 * j + 4 * u + 3]));
     if constexpr (QK) {
-      if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BC);
+      if (masked_at(blk + 1)) apply_mask(sn, (blk + 1) * BC);
       s[0] = sn[0];
       s[1] = sn[1];
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) pp[kb][u] = pb[kb][u];
   };
 
-  // Last product: O += P(T-1) V(T-1) from the V stage vr (k-slot (h, e) of
-  // each 16-key step is key 32 kb + 16 u + 8 h + e on both operands).
-  auto final_pv = [&](const uint4* vr, const bf16x8_t (&pp)[2][2]) {
-    wait_copies_and_sync();
-    i16x4_t vf[VPF][2];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) {
-      vf[i][0] = vread(vr, i, 0);
-      vf[i][1] = vread(vr, i, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const i16x4_t lo = vf[i % VPF][0], hi = vf[i % VPF][1];
-      if (i + VPF < NPV) {
-        vf[i % VPF][0] = vread(vr, i + VPF, 0);
-        vf[i % VPF][1] = vread(vr, i + VPF, 1);
-      }
-      const int db = i % G::NDB;
-      const int u = (i / G::NDB) & 1;
-      const int kb = i / (2 * G::NDB);
-      const bf16x8_t vv = __builtin_bit_cast(
-          bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pp[kb][u],
-                                                         oacc[db], 0, 0, 0);
-    }
-  };
-
-  // ---- prologue: K blocks 0 and 1 into LDS, scores of block 0 ----
-  // Stages by parity of the step t: step t reads K(t+1) from Ks[(t+1) % 2]
-  // and V(t-1) from Vs[(t-1) % 2] and fills Ks[t % 2] with K(t+2) and
-  // Vs[t % 2] with V(t).
+  // ---- prologue: K tiles 0 and 1, V tile 0 into LDS; scores of block 0 --
+  // Stages: tile t lives in Ks[t % 2] / Vs[t % 2].  Step blk reads K block
+  // blk+1 (tile (blk+1)/2, half (blk+1)%2) and V block blk-1; SYNC steps
+  // are the odd ones.  With period 4 in blk:
+  //   blk%4 == 0: K Ks0 half 1, V Vs1 half 1
+  //   blk%4 == 1: K Ks1 half 0, V Vs0 half 0, SYNC: fill Vs1, Ks0
+  //   blk%4 == 2: K Ks1 half 1, V Vs0 half 1
+  //   blk%4 == 3: K Ks0 half 0, V Vs1 half 0, SYNC: fill Vs0, Ks1
   copy_k(0, Ks0);
-  if (ntiles > 1) copy_k(1, Ks1);
+  copy_v(0, Vs0);
+  copy_k(1, Ks1);
   wait_copies_and_sync();
   f32x16_t s[2];
   s[0] = f32x16_t{};
@@ -519,68 +592,63 @@ fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NQK; ++i)
     s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(kfrag(Ks0, i)), qf[i >> 1], s[i & 1], 0, 0, 0);
+        as_bf16x8(kfrag(Ks0, 0, i >> 1)), qf[i & 1][i >> 1], s[i & 1], 0, 0,
+        0);
   if (masked_at(0)) apply_mask(s, 0);
-  {
-    // Reference max from block 0 (every row sees key 0, so m is finite).
-    float mx = s[0][0];
+  // Reference max from block 0 (every row sees key 0, so m is finite for
+  // the rows that exist).
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+  for (int j = 0; j < 2; ++j) {
+    float mx = s[j][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
     mx = half_max(mx);
-    m_run = (mx == -__builtin_inff()) ? mx : mx * c;
+    m_run[j] = (mx == -__builtin_inff()) ? mx : mx * c;
   }
   bf16x8_t pp[2][2];
 
-  // ---- steps 0 .. T-1, then the last product ----
-  const int last = ntiles - 1;
-  if (last == 0) {
-    step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{}, Tag<false>{});
-    final_pv(Vs0, pp);
-  } else {
-    step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{}, Tag<false>{});
-    int t = 1;
-    for (; t + 2 <= last; t += 2) {            // steps t (odd), t + 1 (even)
-      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{}, Tag<true>{});
-      step(t + 1, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{}, Tag<true>{});
-    }
-    if (t < last) {                           // one more odd step
-      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{}, Tag<true>{});
-      ++t;
-    }
-    if (t & 1) {                              // t == last
-      step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<false>{}, Tag<true>{});
-      final_pv(Vs1, pp);
-    } else {
-      step(t, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{}, Tag<true>{});
-      final_pv(Vs0, pp);
-    }
+  using T0 = Tag<false>;
+  using T1 = Tag<true>;
+  // ---- step 0 (no P V yet), then rounds of four steps ----
+  step(0, s, pp, Ks0, Vs1, Ks0, Vs0, Int<1>{}, Int<1>{}, T0{}, T0{});
+  for (int blk = 1; blk <= nsteps; blk += 4) {
+    step(blk, s, pp, Ks1, Vs0, Ks0, Vs1, Int<0>{}, Int<0>{}, T1{}, T1{});
+    step(blk + 1, s, pp, Ks1, Vs0, Ks0, Vs1, Int<1>{}, Int<1>{}, T0{}, T1{});
+    step(blk + 2, s, pp, Ks0, Vs1, Ks1, Vs0, Int<0>{}, Int<0>{}, T1{}, T1{});
+    step(blk + 3, s, pp, Ks0, Vs1, Ks1, Vs0, Int<1>{}, Int<1>{}, T0{}, T1{});
   }
 
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
-  const float l_tot = half_sum(l_run);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    uint16_t* op = static_cast<uint16_t*>(a.o) +
-                   ((static_cast<int64_t>(b) * a.H + hq) * N + qrow) * D;
-    // Accumulator row m <-> d = 32 db + sigma(m): lane half h holds
-    // d = 32 db + 16 u + 8 h + (0..7) in registers 8 u .. 8 u + 7.
+  acc_read_fence();
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
+  for (int j = 0; j < 2; ++j) {
+    const int qrow = qw0 + 32 * j + li;
+    const float l_tot = half_sum(l_run[j]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow < N) {
+      uint16_t* op = static_cast<uint16_t*>(a.o) +
+                     ((static_cast<int64_t>(b) * a.H + hq) * N + qrow) * D;
+      // Accumulator row m <-> d = 32 db + sigma(m): lane half h holds
+      // d = 32 db + 16 u + 8 h + (0..7) in registers 8 u .. 8 u + 7.
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint4 w;
-        w.x = pack_bf16x2(oacc[db][8 * u + 0] * inv, oacc[db][8 * u + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][8 * u + 2] * inv, oacc[db][8 * u + 3] * inv);
-        w.z = pack_bf16x2(oacc[db][8 * u + 4] * inv, oacc[db][8 * u + 5] * inv);
-        w.w = pack_bf16x2(oacc[db][8 * u + 6] * inv, oacc[db][8 * u + 7] * inv);
-        *reinterpret_cast<uint4*>(op + 32 * db + 16 * u + 8 * h) = w;
+      for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x16_t& o = oacc[j][db];
+          uint4 w;
+          w.x = pack_bf16x2(o[8 * u + 0] * inv, o[8 * u + 1] * inv);
+          w.y = pack_bf16x2(o[8 * u + 2] * inv, o[8 * u + 3] * inv);
+          w.z = pack_bf16x2(o[8 * u + 4] * inv, o[8 * u + 5] * inv);
+          w.w = pack_bf16x2(o[8 * u + 6] * inv, o[8 * u + 7] * inv);
+          *reinterpret_cast<uint4*>(op + 32 * db + 16 * u + 8 * h) = w;
+        }
       }
-    }
-    if (h == 0) {
-      const float m_fin = (m_run == -__builtin_inff()) ? 0.f : m_run;
-      float* lp = a.lse + (static_cast<int64_t>(b) * a.H + hq) * N + qrow;
-      *lp = (l_tot > 0.f) ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f
-                          : -__builtin_inff();
+      if (h == 0) {
+        const float m_fin = (m_run[j] == -__builtin_inff()) ? 0.f : m_run[j];
+        float* lp = a.lse + (static_cast<int64_t>(b) * a.H + hq) * N + qrow;
+        *lp = (l_tot > 0.f) ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f
+                            : -__builtin_inff();
+      }
     }
   }
 }
