@@ -312,6 +312,22 @@ fwd_bf16_kernel(const FwdArgs a) {
     for (int i = 0; i < G::VPW; ++i)
       copy_to_lds(rs, stage + 64 * (wave + NWAVE * i), voff0, 4096u * i);
   };
+  // Copy n of the NCOPY copies a wave issues per tile pair: V copies first,
+  // then K copies (the last K window only on the waves that have one).
+  constexpr int NCOPY = G::VPW + G::KPW;
+  auto copy_nth = [&](int n, __amdgpu_buffer_rsrc_t rk,
+                      __amdgpu_buffer_rsrc_t rv, const uint4* kw,
+                      const uint4* vw) {
+    if (n < G::VPW) {
+      copy_to_lds(rv, vw + 64 * (wave + NWAVE * n), voff0, 4096u * n);
+    } else {
+      const int i = n - G::VPW;
+      if (i < kinst)
+        copy_to_lds(rk, kw + 64 * (wave + NWAVE * i),
+                    i < KREG ? (koff2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu
+                             : k_offset(i));
+    }
+  };
 
   // ---- per-lane LDS read offsets (bytes) ----
   //   K (A operand of S^T): row sigma(li) of the 32-key half kh of a stage,
@@ -446,6 +462,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     mfma_pv_acc(v8, pb, acc);
   };
 
+  static_assert(NCOPY <= NSL, "one copy per issue slot");
   // Step blk of the three-stage pipeline.  On entry `s` holds the (masked)
   // scores of block blk and `pp` the settled P of block blk-1.  The K stage
   // kr (32-key half KH) holds block blk+1, the V stage vr (half VH) block
@@ -465,12 +482,13 @@ fwd_bf16_kernel(const FwdArgs a) {
     constexpr bool SYNC = decltype(sync_tag)::value;
     constexpr bool QK = true;
     constexpr bool PV = decltype(pv_tag)::value;
-    if constexpr (SYNC) {
-      wait_copies_and_sync();
-      const int tile = (blk - 1) >> 1;
-      copy_v(tile + 1, vw);
-      copy_k(tile + 2, kw);
-    }
+    // SYNC steps start the copies of tiles (blk-1)/2 + 2 (K, into kw) and
+    // (blk-1)/2 + 1 (V, into vw), one per issue slot, so that their issue
+    // overlaps the matrix work.
+    const int tile = (blk - 1) >> 1;
+    const auto rk = rsrc_at(kp, (tile + 2) * BT);
+    const auto rv = rsrc_at(vp, (tile + 1) * BT);
+    if constexpr (SYNC) wait_copies_and_sync();
     const float mu0 = m_run[0], mu1 = m_run[1];
     uint4 kf[KPF];
     i16x4_t vf[VPF][2];
@@ -508,6 +526,9 @@ fwd_bf16_kernel(const FwdArgs a) {
         }
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(kcur), qf[i & 1][i >> 1], sn[i & 1], 0, 0, 0);
+      }
+      if constexpr (SYNC) {
+        if (i < NCOPY) copy_nth(i, rk, rv, kw, vw);
       }
       __builtin_amdgcn_sched_barrier(0);
       float e[PPS][2];
