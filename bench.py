@@ -126,8 +126,10 @@ def _cpu_baseline(w, host, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=25,
+                    help="untimed launches first (the clock settles over "
+                         "the first ~10 launches of a burst)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true",
@@ -177,7 +179,7 @@ def main() -> int:
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
             m = _time_launches(lambda: fa.forward(qq, kk, vv, causal=ww.causal,
-                                                  out=oo, lse=ll), 10, 3)
+                                                  out=oo, lse=ll), 20, 20)
             t = ww.flops / (m * 1e-3) / 1e12
             extras[name] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
                             "frac_of_bf16_peak": round(t / BF16_PEAK_TFLOPS, 4)}
@@ -197,12 +199,12 @@ def main() -> int:
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
             m = _time_launches(lambda: fa.forward_fp8(q8, k8, v8, desc,
-                                                      out=oo, lse=ll), 10, 3)
+                                                      out=oo, lse=ll), 20, 20)
             t = ww.flops / (m * 1e-3) / 1e12
             key = "fp8_n8192" + ("_hadamard" if rot else "")
             extras[key] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
                            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
-        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 10, 3)
+        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20)
         nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
         extras["fp8_quantize_hadamard_per_tensor"] = {
             "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
