@@ -252,7 +252,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d128"),
-            "kernel": "fwd_bf16_kernel<128, false>",
+            "kernel": "fwd_bf16_kernel<128, false, 2>",
             "flops_per_launch": w.flops,
         },
         "cpu_baseline": cpu,
