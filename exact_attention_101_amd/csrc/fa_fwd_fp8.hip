@@ -10,13 +10,31 @@
 //     device memory (no host synchronisation).  The score scale folds in
 //     dQ * dK; dV multiplies the output in the epilogue.
 //   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4
-//     with neutral (2^0) block scales, fp32 accumulation.
-//   * P is rounded to e4m3 after multiplying by 2^8 (p' = exp2(t - m + 8),
-//     at most 256 < 448), which keeps small weights out of the e4m3
-//     subnormal range; the running denominator carries the same factor, so
-//     it cancels in O = acc / l and is removed from the LSE.
-//   * Q stays in registers; K and V tiles of 64 keys are double-buffered in
-//     LDS; V^T operands come from the transposing ds_read_b64_tr_b8.
+//     with neutral (2^0) block scales, fp32 accumulation.  Each lane owns
+//     one query; the lane's 32 scores of a 64-key tile, rounded to e4m3, are
+//     exactly its 32-byte B operand of the P V product (K rows in sigma
+//     order, fa_common.h), and the V^T operand comes from the transposing
+//     ds_read_b64_tr_b8.
+//   * Workgroup = 8 waves of 32 query rows (BR = 256), two waves per SIMD:
+//     with fp8 the matrix work per score halves, so the vector work of the
+//     softmax needs the issue slots of two waves.  K and V tiles of 64 keys
+//     go from HBM/L2 straight into LDS with buffer_load_dwordx4 ... lds (one
+//     1 KB window of each per wave), double-buffered.
+//   * A three-stage software pipeline runs in every step t: one issue slot
+//     per MFMA pair, the scores MFMA of tile t+1, p = exp2(S c - m + 8) for
+//     four score pairs of tile t, the P V MFMA of tile t-1, then the e4m3
+//     packs and lane sums of those pairs (the intra-group overlap of the
+//     FlashAttention-3 summary, section «Assincronia»).
+//   * P is stored as p * 2^8 (keeps small weights out of the e4m3 subnormal
+//     range), which must stay at most 448.  The running reference value m
+//     need not be the row maximum (any m gives the same softmax; the shift
+//     cancels between numerator and denominator).  A lane sum of the tile's
+//     p * 2^8 at most 448 guarantees every element is; only if a lane sum
+//     exceeds that (or is inf / NaN, as with the initial m = -inf) does the
+//     wave take the exact step: m moves to the tile's row maximum plus an
+//     integer shift chosen so the lane sums come out near 448/4, O and l
+//     are rescaled, and P is formed again.  The denominator carries the same
+//     2^8, so it cancels in O = acc / l and is removed from the LSE.
 #include "fa_common.h"
 
 namespace fa {
@@ -24,28 +42,37 @@ namespace fa {
 namespace {
 
 constexpr int D = 128;
-constexpr int BR = 128;
-constexpr int BC = 64;
-constexpr int NTHR = 256;
+constexpr int NWAVE = 8;
+constexpr int BR = 32 * NWAVE;       // query rows per workgroup
+constexpr int BT = 64;               // keys per tile (= per step)
+constexpr int NTHR = 64 * NWAVE;
 constexpr int NCH = D / 16;          // 16-byte chunks per row (8)
-constexpr int KROWS = NTHR / NCH;    // rows per load pass (32)
-constexpr int KPASS = BC / KROWS;    // passes per tile (2)
 constexpr float P_SHIFT = 8.0f;      // P is stored as p * 2^8
+constexpr float P_SUM_MAX = 448.0f;  // e4m3 largest finite value
+constexpr float P_SUM_AIM = 112.0f;  // lane sum aimed at by the exact step
 
-// K tile: lane i reads row sigma(i) (+32 kb); XOR term depends on i only.
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+
+template <bool V>
+struct Tag {
+  static constexpr bool value = V;
+};
+
+// K tile [key][d] bytes: physical 16-byte chunk of (row r, chunk c).  The
+// reading lane i uses row r = sigma(i) (+32 kb), so the XOR term depends on
+// the lane only and 16 lanes reading the same logical chunk hit 16
+// different 4-bank groups.
 __device__ __forceinline__ int kswz(int r, int c) {
   const int t = sigma(r & 31);
   return c ^ ((t & 7) ^ ((t >> 3) & 1));
 }
 
-// V tile: the 8 key rows of one transposing read differ in (r % 2,
-// (r >> 1) % 4); XOR-ing the 32-byte segment with (r >> 1) % 4 spreads them
-// over all banks.
+// V tile [key][d] bytes: the 8 key rows of one transposing read differ in
+// (r % 2, (r >> 1) % 4); XOR-ing the 32-byte segment with (r >> 1) % 4
+// spreads them over all banks.
 __device__ __forceinline__ int vswz(int r, int c) {
   return c ^ (2 * ((r >> 1) & 3));
 }
-
-typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 
 // Transposing 8-bit LDS read: in each group of 16 lanes, lanes 2R and 2R+1
 // supply 8 consecutive bytes each (row R = 16 bytes), and output lane i gets
@@ -60,15 +87,56 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two fp32 values to e4m3 (RNE, saturating) into the low (hi = 0) or high
+// (hi = 1) 16 bits of `old`.
+__device__ __forceinline__ int pack_fp8x2(float a, float b, int old, int hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x16_t mfma_f8(const i32x8_t& a,
+                                            const i32x8_t& b,
+                                            const f32x16_t& c) {
+  // cbsz = blgp = 0: both operands e4m3; scale exponents 127 = 2^0.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0,
+                                                         127, 0, 127);
+}
+
+// One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset bytes) into
+// LDS at `dst` + 16 * lane.  Offsets past the descriptor's size read zeros.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
+                                            const uint4* dst,
+                                            uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset, 0, 0,
+      0);
+}
+
 template <bool CAUSAL>
-__global__ void __launch_bounds__(NTHR, 2)
+__global__ void __launch_bounds__(NTHR, 1)
 fwd_fp8_kernel(const FwdArgs a) {
-  __shared__ uint4 Ks[2][BC * NCH];   // [key][d] bytes, swizzled
-  __shared__ uint4 Vs[2][BC * NCH];   // [key][d] bytes, swizzled
+  __shared__ uint4 Ks0[BT * NCH];
+  __shared__ uint4 Ks1[BT * NCH];
+  __shared__ uint4 Vs0[BT * NCH];
+  __shared__ uint4 Vs1[BT * NCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int li = lane & 31;
   const int h = lane >> 5;
 
@@ -90,10 +158,11 @@ fwd_fp8_kernel(const FwdArgs a) {
     dv = a.descale[2];
   }
   // Scores enter exp2 as S * c with c = |scale| dQ dK log2(e); a negative
-  // product is handled by negating Q's codes (sign bit) on load.
+  // product is handled by negating Q's codes (sign bit) on load.  c is
+  // floored so that a masked score (-inf) always gives p = 0.
   const float cs = a.scale * dq * dk * 1.4426950408889634f;
   const bool neg = cs < 0.f;
-  const float c = fabsf(cs);
+  const float c = fmaxf(fabsf(cs), 1e-30f);
 
   const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
                       (static_cast<int64_t>(b) * a.H + hq) * N * D;
@@ -120,161 +189,242 @@ fwd_fp8_kernel(const FwdArgs a) {
     }
   }
 
-  // Staging registers: thread tid moves 16-byte chunk (tid % NCH) of rows
-  // tid / NCH and tid / NCH + 32 of both K and V (KPASS == 2).
-  static_assert(KPASS == 2, "staging below is written for two passes");
-  uint4 k0s, k1s, v0s, v1s;
-  const int kc = tid % NCH;
-  const int kr = tid / NCH;
+  // ---- tile copies: wave w fills 64-slot window w of each stage ----
+  // Lane L writes physical slot 64 w + L = row * NCH + physical chunk; the
+  // logical chunk is recovered with the (involutive) swizzle.
+  uint32_t koff, voff;
+  {
+    const int slot = 64 * wave + lane;
+    const int r = slot / NCH, p = slot % NCH;
+    koff = static_cast<uint32_t>(r * D + 16 * kswz(r, p));
+    voff = static_cast<uint32_t>(r * D + 16 * vswz(r, p));
+  }
+  static_assert(BT * NCH == 64 * NWAVE, "one copy window per wave");
 
-  auto load_tile = [&](int kv0) {
-    // Rows past the end read row N-1 (always in bounds).  Their scores are
-    // masked; their V values are zeroed so that P = 0 times V stays 0.
-    const int r0 = kv0 + kr, r1 = r0 + KROWS;
-    const int64_t o0 = static_cast<int64_t>(min(r0, N - 1)) * D + 16 * kc;
-    const int64_t o1 = static_cast<int64_t>(min(r1, N - 1)) * D + 16 * kc;
-    k0s = *reinterpret_cast<const uint4*>(kp + o0);
-    k1s = *reinterpret_cast<const uint4*>(kp + o1);
-    v0s = keep_if(*reinterpret_cast<const uint4*>(vp + o0), r0 < N);
-    v1s = keep_if(*reinterpret_cast<const uint4*>(vp + o1), r1 < N);
-  };
-  auto store_tile = [&](int buf) {
-    const int r0 = kr, r1 = kr + KROWS;
-    Ks[buf][r0 * NCH + kswz(r0, kc)] = k0s;
-    Ks[buf][r1 * NCH + kswz(r1, kc)] = k1s;
-    Vs[buf][r0 * NCH + vswz(r0, kc)] = v0s;
-    Vs[buf][r1 * NCH + vswz(r1, kc)] = v1s;
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
+  const int ntiles = (kv_end + BT - 1) / BT;
+  // Steps 1 .. nsteps run in pairs; step t ends with O += P(t-1) V(t-1), so
+  // the last real tile is done at step ntiles.  Tiles past the real ones
+  // are virtual: their copies read zeros (the descriptors end at kv_end) and
+  // their scores are masked, so their p are 0.
+  const int nsteps = (ntiles + 1) & ~1;
+
+  auto rsrc_at = [&](const uint8_t* base, int kv0) {
+    const int rows = max(kv_end - kv0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base + static_cast<int64_t>(kv0) * D), 0,
+        rows * D, 0x00020000);
   };
 
-  // Transposed V read, per lane: group g = lane / 16, lanes 2R + j of the
-  // group read key row R (+ tile offsets) at bytes [32 db + 16 (g % 2) + 8 j,
-  // +8).  Output lane i then holds 8 keys of d = 32 db + 16 (g % 2) + i.
+  // ---- LDS read offsets ----
+  //   K fragment (kb, s): row 32 kb + sigma(li), logical chunks 4 h + 2 s
+  //   and 4 h + 2 s + 1.
+  auto kfrag = [&](const uint4* ks, int kb, int s) {
+    const int r = 32 * kb + sigma(li);
+    const uint4* row = ks + r * NCH;
+    const uint4 k0 = row[kswz(r, 4 * h + 2 * s)];
+    const uint4 k1 = row[kswz(r, 4 * h + 2 * s + 1)];
+    return i32x8_t{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                   (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+  };
+  //   Transposed V fragment of d block db: group g = lane / 16, lanes 2R + j
+  //   of the group read key row 16 t8 + 8 h + R at bytes [32 db + 16 (g % 2)
+  //   + 8 j, +8); output lane i then holds 8 keys of d = 32 db + 16 (g % 2)
+  //   + i, for t8 = 0..3 (bytes 8 t8 .. 8 t8 + 7 of the A operand).
   const int tr_g = lane >> 4;
   const int tr_R = (lane >> 1) & 7;
   const int tr_j = lane & 1;
   const int tr_c = 2 * (tr_g & 1) + tr_j;        // 8-byte unit in a 32-d block
+  auto vfrag = [&](const uint4* vs, int db) {
+    int av[8];
+#pragma unroll
+    for (int t8 = 0; t8 < 4; ++t8) {
+      const int r = 16 * t8 + 8 * h + tr_R;
+      const int unit = 4 * db + tr_c;
+      const uint8_t* p = reinterpret_cast<const uint8_t*>(
+                             vs + r * NCH + vswz(r, unit >> 1)) +
+                         8 * (unit & 1);
+      const i32x2_t x = lds_read_tr8(p);
+      av[2 * t8] = x[0];
+      av[2 * t8 + 1] = x[1];
+    }
+    return i32x8_t{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+  };
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run = -__builtin_inff();      // reference, log2 units
+  float l_run = 0.f;                    // this lane's half of sum p * 2^8
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kv0 = t * BC;
-    if (t + 1 < ntiles) load_tile(kv0 + BC);
-
-    const bool skip = CAUSAL && (kv0 > qw0 + 31);
-    if (!skip) {
-      f32x16_t sacc[2];
+  // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
+  auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16_t{};
-        const int r = 32 * kb + sigma(li);
-        const uint4* row = &Ks[buf][r * NCH];
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint4 k0 = row[kswz(r, 4 * h + 2 * s)];
-          const uint4 k1 = row[kswz(r, 4 * h + 2 * s + 1)];
-          const i32x8_t kk = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
-                              (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              kk, qf[s], sacc[kb], 0, 0, 0, 127, 0, 127);
-        }
-      }
-
-      const bool need_mask =
-          (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
-            const bool ok = key < N && (!CAUSAL || key <= qrow);
-            if (!ok) sacc[kb][r] = -__builtin_inff();
-          }
-        }
-      }
-
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * c;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      const float moff = P_SHIFT - m_use;
-
-      // P^T in e4m3: byte e = 16 kb + r of this lane <-> key
-      // 32 kb + 16 (r / 8) + 8 h + r % 8.
-      float psum = 0.f;
-      int pw[8];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s = sacc[w >> 2][4 * (w & 3) + e];
-          p[e] = (s == -__builtin_inff())
-                     ? 0.f
-                     : __builtin_amdgcn_exp2f(fmaf(s, c, moff));
-          psum += p[e];
-        }
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], v, true);
-      }
-      const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3],
-                          pw[4], pw[5], pw[6], pw[7]};
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // O^T += V^T P^T: A operand byte e of lane half h <-> the same key as
-      // the B operand: read t8 (bytes 8 t8 .. 8 t8 + 7) covers keys
-      // 16 t8 + 8 h + R, R = 0..7.
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        int av[8];
-#pragma unroll
-        for (int t8 = 0; t8 < 4; ++t8) {
-          const int r = 16 * t8 + 8 * h + tr_R;
-          const int unit = 4 * db + tr_c;                  // 8-byte unit
-          const uint8_t* p = reinterpret_cast<const uint8_t*>(
-                                 &Vs[buf][r * NCH + vswz(r, unit >> 1)]) +
-                             8 * (unit & 1);
-          const i32x2_t x = lds_read_tr8(p);
-          av[2 * t8] = x[0];
-          av[2 * t8 + 1] = x[1];
-        }
-        const i32x8_t va = {av[0], av[1], av[2], av[3],
-                            av[4], av[5], av[6], av[7]};
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            va, pb, oacc[db], 0, 0, 0, 127, 0, 127);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+        const bool ok = key < N && (!CAUSAL || key <= qrow);
+        if (!ok) s[kb][r] = -__builtin_inff();
       }
     }
+  };
+  auto masked_at = [&](int t) {
+    const int kv0 = t * BT;
+    return (kv0 + BT > N) || (CAUSAL && kv0 + BT - 1 > qw0);
+  };
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+  // P pair pr (0..15) of a lane: scores s[pr / 8][2 (pr % 8) + (0, 1)],
+  // stored as e4m3 bytes 2 pr, 2 pr + 1 of the lane's 32-byte B operand.
+  auto form_p = [&](const f32x16_t (&s)[2], float m_use, int (&pw)[8]) {
+    float sum = 0.f;
+    const float moff = P_SHIFT - m_use;
+#pragma unroll
+    for (int pr = 0; pr < 16; ++pr) {
+      const int kb = pr >> 3, r = 2 * (pr & 7);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
+      pw[pr >> 1] = pack_fp8x2(p0, p1, pw[pr >> 1], pr & 1);
+      sum += p0 + p1;
+    }
+    return sum;
+  };
+
+  // Exact step for a tile whose lane sum of p * 2^8 exceeds 448 or is
+  // inf / NaN: m moves to the tile's row maximum (if larger) plus the
+  // smallest integer shift e >= 0 that brings the larger of the row's two
+  // lane sums to at most 448 / 4; O and l are rescaled, P formed again.
+  // Returns the new lane sum.
+  auto exact_tile = [&](const f32x16_t (&s)[2], int (&pw)[8]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+    mx = half_max(mx);
+    const float m_blk = (mx == -__builtin_inff()) ? mx : mx * c;
+    float m_new = fmaxf(m_run, m_blk);
+    if (m_new != -__builtin_inff()) {
+      const float sum = form_p(s, m_new, pw);
+      const float ratio = half_max(sum) * (1.0f / P_SUM_AIM);
+      // ratio <= 2^e with e the binary exponent of ratio (frexp form).
+      const int e = ratio > 1.0f ? __builtin_amdgcn_frexp_expf(ratio) : 0;
+      m_new += static_cast<float>(e);
+    }
+    const float alpha = (m_new == -__builtin_inff())
+                            ? 1.0f
+                            : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    // A row with no visible key so far keeps m = -inf; its p are all 0.
+    return form_p(s, (m_new == -__builtin_inff()) ? 0.f : m_new, pw);
+  };
+
+  auto wait_copies_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
     __syncthreads();
+  };
+
+  // Step t of the three-stage pipeline.  On entry `s` holds the (masked)
+  // scores of tile t and `pp` the settled P of tile t-1.  K stage kr holds
+  // tile t+1, V stage vr tile t-1.  The step first waits for the copies of
+  // the previous step, then starts those of tiles t+2 (K, into kw) and t
+  // (V, into vw).  Slot i: scores MFMA i (key block i % 2, d step i / 2) of
+  // tile t+1; p for pairs 4 i .. 4 i + 3 of tile t; P V MFMA of d block i
+  // for tile t-1; e4m3 packs and lane sums of those pairs.
+  auto step = [&](int t, f32x16_t (&s)[2], i32x8_t& pp, const uint4* kr,
+                  const uint4* vr, const uint4* kw, const uint4* vw,
+                  auto pv_tag) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    const auto rk = rsrc_at(kp, (t + 2) * BT);
+    const auto rv = rsrc_at(vp, t * BT);
+    wait_copies_and_sync();
+    const float moff = P_SHIFT - m_run;
+    i32x8_t kf = kfrag(kr, 0, 0);
+    i32x8_t vf;
+    if constexpr (PV) vf = vfrag(vr, 0);
+    f32x16_t sn[2];
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+    int pw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pw[i] = 0;
+    float ls0 = 0.f, ls1 = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8_t kcur = kf;
+      if (i + 1 < 4) kf = kfrag(kr, (i + 1) & 1, (i + 1) >> 1);
+      sn[i & 1] = mfma_f8(kcur, qf[i >> 1], sn[i & 1]);
+      if (i == 0) copy_to_lds(rv, vw + 64 * wave, voff);
+      if (i == 1) copy_to_lds(rk, kw + 64 * wave, koff);
+      __builtin_amdgcn_sched_barrier(0);
+      float e[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pr = 4 * i + q;
+        const int kb = pr >> 3, r = 2 * (pr & 7);
+        e[q][0] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
+        e[q][1] = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
+        asm volatile("" : "+v"(e[q][0]), "+v"(e[q][1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PV) {
+        const i32x8_t vcur = vf;
+        if (i + 1 < 4) vf = vfrag(vr, i + 1);
+        oacc[i] = mfma_f8(vcur, pp, oacc[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pr = 4 * i + q;
+        pw[pr >> 1] = pack_fp8x2(e[q][0], e[q][1], pw[pr >> 1], pr & 1);
+        if (q & 1) ls1 += e[q][0] + e[q][1]; else ls0 += e[q][0] + e[q][1];
+        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Accept P of tile t (every element is at most the lane sum, so a sum
+    // <= 448 keeps every e4m3 value finite) or take the exact step first,
+    // then add the tile to l.
+    float ls = ls0 + ls1;
+    const bool bad = !(ls <= P_SUM_MAX);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_tile(s, pw);  // rare
+    l_run += ls;
+    pp = i32x8_t{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BT);
+    s[0] = sn[0];
+    s[1] = sn[1];
+  };
+
+  // ---- prologue: K tiles 0 and 1 into LDS, scores of tile 0 ----
+  // Stages: tile u lives in Ks[u % 2] / Vs[u % 2]; step t reads K(t+1) and
+  // V(t-1), both from stage (t+1) % 2, and fills stage t % 2.
+  copy_to_lds(rsrc_at(kp, 0), Ks0 + 64 * wave, koff);
+  copy_to_lds(rsrc_at(kp, BT), Ks1 + 64 * wave, koff);
+  wait_copies_and_sync();
+  f32x16_t s[2];
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    s[i & 1] = mfma_f8(kfrag(Ks0, i & 1, i >> 1), qf[i >> 1], s[i & 1]);
+  if (masked_at(0)) apply_mask(s, 0);
+  i32x8_t pp = {};
+
+  // Step 0 finds m = -inf, so its sums are inf / NaN and it takes the exact
+  // step, which sets the reference from tile 0.
+  step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{});
+  for (int t = 1; t <= nsteps; t += 2) {
+    step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{});
+    step(t + 1, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{});
   }
 
   // Epilogue.  Accumulator row m <-> d = 32 db + m: lane half h holds runs
   // of 4 consecutive d at 32 db + 8 (r / 4) + 4 h.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
   const float inv = (l_tot > 0.f) ? dv / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* op = static_cast<uint16_t*>(a.o) +
@@ -304,6 +454,10 @@ hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
   a.nqb = (a.N + BR - 1) / BR;
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  // Per-(batch, KV head) byte ranges are addressed by 32-bit buffer
+  // offsets.
+  if (static_cast<long long>(a.N) * D > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
   if (causal) {

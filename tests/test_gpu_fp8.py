@@ -50,14 +50,14 @@ def test_quantize_zero_tensor():
     np.testing.assert_array_equal(ad.cpu().numpy(), [0.0, 1.0])
 
 
-def _fp8_forward(q, k, v, signs, causal, Hkv=None):
+def _fp8_forward(q, k, v, signs, causal, Hkv=None, scale=None):
     import torch
     import exact_attention_101_amd as fa
     q8, sq = _quant(q, signs)
     k8, sk = _quant(k, signs)
     v8, sv = _quant(v, None)
     desc = torch.stack([sq[1], sk[1], sv[1]]).contiguous()
-    o, lse = fa.forward_fp8(q8, k8, v8, desc, causal=causal)
+    o, lse = fa.forward_fp8(q8, k8, v8, desc, causal=causal, scale=scale)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -106,3 +106,33 @@ def test_fp8_full_size_sampled(rotate):
           f"vs unquantised inputs {rel_exact:.3e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert rel <= FP8_REL_L2_TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", ["zero_q", "large_scale", "rising_keys"])
+def test_fp8_reference_moves(case, causal):
+    """Inputs that drive the kernel's reference-maximum logic: uniform
+    weights (all-zero Q: every lane sum of the scaled p exceeds the e4m3
+    range until the reference moves up), a large scale (peaky rows, scores
+    far above any earlier reference) and keys whose norm rises along the
+    sequence (the row maximum keeps growing mid-row).  Against the oracle on
+    the dequantised inputs, same scale."""
+    B, H, Hkv, N, d = 1, 2, 2, 1000, 128
+    q, k, v = workloads.qkv(B, H, Hkv, N, d, 7100, outliers=False)
+    scale = d ** -0.5
+    if case == "zero_q":
+        q = np.zeros_like(q)
+    elif case == "large_scale":
+        scale = 12.0 * d ** -0.5
+    else:
+        ramp = np.linspace(0.25, 4.0, N, dtype=np.float32)[None, None, :, None]
+        k = (k * ramp).astype(np.float32)
+    o, lse = _fp8_forward(q, k, v, None, causal, scale=scale)
+    qd, kd, vd = _oracle_deq(q, None), _oracle_deq(k, None), _oracle_deq(v, None)
+    ro, rl = oracle.attention(qd, kd, vd, causal=causal, scale=scale)
+    rel = np.linalg.norm(o - ro) / np.linalg.norm(ro)
+    el = np.abs(lse - rl).max()
+    print(f"fp8 {case}: rel-L2={rel:.3e} max|dLSE|={el:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert rel <= FP8_REL_L2_TOL
+    assert el <= 2e-2
