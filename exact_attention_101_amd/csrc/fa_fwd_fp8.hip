@@ -25,16 +25,21 @@
 //     four score pairs of tile t, the P V MFMA of tile t-1, then the e4m3
 //     packs and lane sums of those pairs (the intra-group overlap of the
 //     FlashAttention-3 summary, section «Assincronia»).
-//   * P is stored as p * 2^8 (keeps small weights out of the e4m3 subnormal
-//     range), which must stay at most 448.  The running reference value m
-//     need not be the row maximum (any m gives the same softmax; the shift
-//     cancels between numerator and denominator).  A lane sum of the tile's
-//     p * 2^8 at most 448 guarantees every element is; only if a lane sum
-//     exceeds that (or is inf / NaN, as with the initial m = -inf) does the
-//     wave take the exact step: m moves to the tile's row maximum plus an
-//     integer shift chosen so the lane sums come out near 448/4, O and l
-//     are rescaled, and P is formed again.  The denominator carries the same
-//     2^8, so it cancels in O = acc / l and is removed from the LSE.
+//   * P is stored as p * 2^8 in e4m3 (keeps small weights out of the
+//     subnormal range), which must stay at most 448.  O and l are kept
+//     relative to a per-row base m0 (block 0's row maximum) and are never
+//     rescaled: tile t forms p against m0 + E_t, where E_t is the smallest
+//     integer (never decreasing) that keeps the tile's row maximum within
+//     log2(448/256) of it, and the P V MFMA takes the per-lane block scale
+//     2^E_t of the f8f6f4 instruction, so O accumulates p * 2^8 * 2^E_t
+//     relative to m0 exactly.  Two row sums follow it, each adding the
+//     tile's lane sum times 2^E_t: lq over the e4m3 values the product used
+//     (O = acc / lq, so a row whose weight sits on one key is not off by that
+//     key's rounding, up to 2^-4) and l over the fp32 p before rounding (the
+//     LSE).  Both carry the same 2^8, which cancels in O and is removed from
+//     the LSE.  Only if E passes 64 (scores rising more than 64
+//     log2 units above block 0) are O and l renormalised, to keep fp32
+//     headroom.
 #include "fa_common.h"
 
 namespace fa {
@@ -48,8 +53,10 @@ constexpr int BT = 64;               // keys per tile (= per step)
 constexpr int NTHR = 64 * NWAVE;
 constexpr int NCH = D / 16;          // 16-byte chunks per row (8)
 constexpr float P_SHIFT = 8.0f;      // P is stored as p * 2^8
-constexpr float P_SUM_MAX = 448.0f;  // e4m3 largest finite value
-constexpr float P_SUM_AIM = 112.0f;  // lane sum aimed at by the exact step
+// p * 2^8 <= 448 (largest finite e4m3) when the score is at most
+// log2(448 / 256) = 0.807 log2 units above the reference.
+constexpr float P_HEADROOM = 0.8f;
+constexpr int E_RENORM = 64;         // renormalise O, l beyond this shift
 
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 
@@ -94,6 +101,15 @@ __device__ __forceinline__ int pack_fp8x2(float a, float b, int old, int hi) {
             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
+// acc + the two e4m3 values in the low (hi = 0) or high (hi = 1) 16 bits of
+// w: decoded exactly to bf16, then a bf16 dot with (1, 1) into fp32.
+__device__ __forceinline__ float add_fp8x2(int w, int hi, float acc) {
+  const bf16x2_t x = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
                                                   __float_as_uint(x), false,
@@ -114,6 +130,15 @@ __device__ __forceinline__ f32x16_t mfma_f8(const i32x8_t& a,
   // cbsz = blgp = 0: both operands e4m3; scale exponents 127 = 2^0.
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0,
                                                          127, 0, 127);
+}
+// Same with the B operand scaled by 2^(eb - 127) (E8M0 block scale, one per
+// lane: each lane's 32 k-values of its column).
+__device__ __forceinline__ f32x16_t mfma_f8_bscale(const i32x8_t& a,
+                                                   const i32x8_t& b,
+                                                   const f32x16_t& c,
+                                                   int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0,
+                                                         127, 0, eb);
 }
 
 // One 64-lane copy of 16 bytes per lane from `rsrc` (+ voffset bytes) into
@@ -254,8 +279,10 @@ fwd_fp8_kernel(const FwdArgs a) {
   f32x16_t oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();      // reference, log2 units
-  float l_run = 0.f;                    // this lane's half of sum p * 2^8
+  float m0 = 0.f;                       // per-row base, log2 units
+  int e_cur = 0;                        // E of the tile whose P is formed
+  float l_run = 0.f;                    // this lane's half of sum p*2^8*2^E
+  float lq_run = 0.f;                   // same over the e4m3-rounded p*2^8
 
   // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
   auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
@@ -274,52 +301,28 @@ fwd_fp8_kernel(const FwdArgs a) {
     return (kv0 + BT > N) || (CAUSAL && kv0 + BT - 1 > qw0);
   };
 
-  // P pair pr (0..15) of a lane: scores s[pr / 8][2 (pr % 8) + (0, 1)],
-  // stored as e4m3 bytes 2 pr, 2 pr + 1 of the lane's 32-byte B operand.
-  auto form_p = [&](const f32x16_t (&s)[2], float m_use, int (&pw)[8]) {
-    float sum = 0.f;
-    const float moff = P_SHIFT - m_use;
+  // Row maximum of a tile's (masked) scores, both lane halves; -inf if
+  // every key of the tile is hidden from the row.
+  auto tile_max = [&](const f32x16_t (&s)[2]) {
+    float m[8];
 #pragma unroll
-    for (int pr = 0; pr < 16; ++pr) {
-      const int kb = pr >> 3, r = 2 * (pr & 7);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
-      pw[pr >> 1] = pack_fp8x2(p0, p1, pw[pr >> 1], pr & 1);
-      sum += p0 + p1;
+    for (int i = 0; i < 8; ++i) {
+      const int j = 4 * i;
+      m[i] = fmaxf(fmaxf(s[j >> 4][j & 15], s[(j + 1) >> 4][(j + 1) & 15]),
+                   fmaxf(s[(j + 2) >> 4][(j + 2) & 15],
+                         s[(j + 3) >> 4][(j + 3) & 15]));
     }
-    return sum;
+    const float mx = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])),
+                           fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+    return half_max(mx);
   };
-
-  // Exact step for a tile whose lane sum of p * 2^8 exceeds 448 or is
-  // inf / NaN: m moves to the tile's row maximum (if larger) plus the
-  // smallest integer shift e >= 0 that brings the larger of the row's two
-  // lane sums to at most 448 / 4; O and l are rescaled, P formed again.
-  // Returns the new lane sum.
-  auto exact_tile = [&](const f32x16_t (&s)[2], int (&pw)[8]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
-    mx = half_max(mx);
-    const float m_blk = (mx == -__builtin_inff()) ? mx : mx * c;
-    float m_new = fmaxf(m_run, m_blk);
-    if (m_new != -__builtin_inff()) {
-      const float sum = form_p(s, m_new, pw);
-      const float ratio = half_max(sum) * (1.0f / P_SUM_AIM);
-      // ratio <= 2^e with e the binary exponent of ratio (frexp form).
-      const int e = ratio > 1.0f ? __builtin_amdgcn_frexp_expf(ratio) : 0;
-      m_new += static_cast<float>(e);
-    }
-    const float alpha = (m_new == -__builtin_inff())
-                            ? 1.0f
-                            : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    // A row with no visible key so far keeps m = -inf; its p are all 0.
-    return form_p(s, (m_new == -__builtin_inff()) ? 0.f : m_new, pw);
+  // E for a tile with row maximum mx (raw score): the smallest integer,
+  // not below the previous one, with mx * c <= m0 + E + P_HEADROOM.
+  auto next_e = [&](float mx, int e_prev) {
+    if (mx == -__builtin_inff()) return e_prev;
+    const float need = ceilf(mx * c - m0 - P_HEADROOM);
+    return need > static_cast<float>(e_prev) ? static_cast<int>(need)
+                                              : e_prev;
   };
 
   auto wait_copies_and_sync = [&]() {
@@ -334,14 +337,15 @@ fwd_fp8_kernel(const FwdArgs a) {
   // (V, into vw).  Slot i: scores MFMA i (key block i % 2, d step i / 2) of
   // tile t+1; p for pairs 4 i .. 4 i + 3 of tile t; P V MFMA of d block i
   // for tile t-1; e4m3 packs and lane sums of those pairs.
-  auto step = [&](int t, f32x16_t (&s)[2], i32x8_t& pp, const uint4* kr,
-                  const uint4* vr, const uint4* kw, const uint4* vw,
-                  auto pv_tag) {
+  auto step = [&](int t, f32x16_t (&s)[2], i32x8_t& pp, int& e_pp,
+                  const uint4* kr, const uint4* vr, const uint4* kw,
+                  const uint4* vw, auto pv_tag) {
     constexpr bool PV = decltype(pv_tag)::value;
     const auto rk = rsrc_at(kp, (t + 2) * BT);
     const auto rv = rsrc_at(vp, t * BT);
     wait_copies_and_sync();
-    const float moff = P_SHIFT - m_run;
+    const float moff = P_SHIFT - (m0 + static_cast<float>(e_cur));
+    const int eb = 127 + e_pp;          // 2^E of the P being multiplied
     i32x8_t kf = kfrag(kr, 0, 0);
     i32x8_t vf;
     if constexpr (PV) vf = vfrag(vr, 0);
@@ -351,7 +355,7 @@ fwd_fp8_kernel(const FwdArgs a) {
     int pw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) pw[i] = 0;
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls0 = 0.f, ls1 = 0.f, lq0 = 0.f, lq1 = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -374,7 +378,7 @@ fwd_fp8_kernel(const FwdArgs a) {
       if constexpr (PV) {
         const i32x8_t vcur = vf;
         if (i + 1 < 4) vf = vfrag(vr, i + 1);
-        oacc[i] = mfma_f8(vcur, pp, oacc[i]);
+        oacc[i] = mfma_f8_bscale(vcur, pp, oacc[i], eb);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -382,21 +386,41 @@ fwd_fp8_kernel(const FwdArgs a) {
         const int pr = 4 * i + q;
         pw[pr >> 1] = pack_fp8x2(e[q][0], e[q][1], pw[pr >> 1], pr & 1);
         if (q & 1) ls1 += e[q][0] + e[q][1]; else ls0 += e[q][0] + e[q][1];
-        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1));
+      }
+      // l sums the rounded values the P V product uses, so a row whose
+      // weight sits on one key still divides that key's value by itself.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pr = 4 * i + q;
+        if (q & 1) lq1 = add_fp8x2(pw[pr >> 1], pr & 1, lq1);
+        else lq0 = add_fp8x2(pw[pr >> 1], pr & 1, lq0);
+        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1), "+v"(lq0),
+                     "+v"(lq1));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Accept P of tile t (every element is at most the lane sum, so a sum
-    // <= 448 keeps every e4m3 value finite) or take the exact step first,
-    // then add the tile to l.
-    float ls = ls0 + ls1;
-    const bool bad = !(ls <= P_SUM_MAX);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) ls = exact_tile(s, pw);  // rare
-    l_run += ls;
+    l_run += __builtin_ldexpf(ls0 + ls1, e_cur);
+    lq_run += __builtin_ldexpf(lq0 + lq1, e_cur);
     pp = i32x8_t{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    e_pp = e_cur;
     if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BT);
     s[0] = sn[0];
     s[1] = sn[1];
+    e_cur = next_e(tile_max(s), e_cur);
+    if (__builtin_amdgcn_ballot_w64(e_cur > E_RENORM) != 0) {   // rare
+      // Move the base up by E: O, l and the pending P's scale follow.
+      const int sh = e_cur;
+      const float f = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
+      l_run *= f;
+      lq_run *= f;
+      m0 += static_cast<float>(sh);
+      e_pp = max(e_pp - sh, -127);
+      e_cur = 0;
+    }
   };
 
   // ---- prologue: K tiles 0 and 1 into LDS, scores of tile 0 ----
@@ -412,20 +436,28 @@ fwd_fp8_kernel(const FwdArgs a) {
   for (int i = 0; i < 4; ++i)
     s[i & 1] = mfma_f8(kfrag(Ks0, i & 1, i >> 1), qf[i >> 1], s[i & 1]);
   if (masked_at(0)) apply_mask(s, 0);
+  {
+    // Base from tile 0 (every row sees key 0, so it is finite for the rows
+    // that exist).
+    const float mx = tile_max(s);
+    m0 = (mx == -__builtin_inff()) ? 0.f : mx * c;
+  }
   i32x8_t pp = {};
+  int e_pp = 0;
 
-  // Step 0 finds m = -inf, so its sums are inf / NaN and it takes the exact
-  // step, which sets the reference from tile 0.
-  step(0, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{});
+  step(0, s, pp, e_pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{});
   for (int t = 1; t <= nsteps; t += 2) {
-    step(t, s, pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{});
-    step(t + 1, s, pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{});
+    step(t, s, pp, e_pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{});
+    step(t + 1, s, pp, e_pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{});
   }
 
   // Epilogue.  Accumulator row m <-> d = 32 db + m: lane half h holds runs
   // of 4 consecutive d at 32 db + 8 (r / 4) + 4 h.
+  // O divides by the sum of the weights it was built from (the e4m3 values);
+  // the LSE takes the sum of the unrounded p.
   const float l_tot = half_sum(l_run);
-  const float inv = (l_tot > 0.f) ? dv / l_tot : 0.f;
+  const float lq_tot = half_sum(lq_run);
+  const float inv = (lq_tot > 0.f) ? dv / lq_tot : 0.f;
   if (qrow < N) {
     uint16_t* op = static_cast<uint16_t*>(a.o) +
                    ((static_cast<int64_t>(b) * a.H + hq) * N + qrow) * D;
@@ -442,7 +474,7 @@ fwd_fp8_kernel(const FwdArgs a) {
     if (h == 0) {
       float* lp = a.lse + (static_cast<int64_t>(b) * a.H + hq) * N + qrow;
       *lp = (l_tot > 0.f)
-                ? (m_run + __log2f(l_tot) - P_SHIFT) * 0.69314718055994531f
+                ? (m0 + __log2f(l_tot) - P_SHIFT) * 0.69314718055994531f
                 : -__builtin_inff();
     }
   }

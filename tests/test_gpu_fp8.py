@@ -109,14 +109,17 @@ def test_fp8_full_size_sampled(rotate):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("case", ["zero_q", "large_scale", "rising_keys"])
+@pytest.mark.parametrize("case", ["zero_q", "large_scale", "rising_keys",
+                                  "rising_large"])
 def test_fp8_reference_moves(case, causal):
-    """Inputs that drive the kernel's reference-maximum logic: uniform
-    weights (all-zero Q: every lane sum of the scaled p exceeds the e4m3
-    range until the reference moves up), a large scale (peaky rows, scores
-    far above any earlier reference) and keys whose norm rises along the
-    sequence (the row maximum keeps growing mid-row).  Against the oracle on
-    the dequantised inputs, same scale."""
+    """Inputs that drive the kernel's per-tile reference (block 0's row
+    maximum plus a whole power of two that only grows): uniform weights
+    (all-zero Q: the reference never moves and every p is 1), a large scale
+    (peaky rows, jumps of many powers of two), keys whose norm rises along
+    the sequence (the reference keeps moving mid-row) and both together
+    (scores rise well over 64 log2 units above block 0, so O and l are
+    renormalised mid-row, several times).  Against the oracle on the
+    dequantised inputs, same scale."""
     B, H, Hkv, N, d = 1, 2, 2, 1000, 128
     q, k, v = workloads.qkv(B, H, Hkv, N, d, 7100, outliers=False)
     scale = d ** -0.5
@@ -125,6 +128,8 @@ def test_fp8_reference_moves(case, causal):
     elif case == "large_scale":
         scale = 12.0 * d ** -0.5
     else:
+        if case == "rising_large":
+            scale = 12.0 * d ** -0.5
         ramp = np.linspace(0.25, 4.0, N, dtype=np.float32)[None, None, :, None]
         k = (k * ramp).astype(np.float32)
     o, lse = _fp8_forward(q, k, v, None, causal, scale=scale)
