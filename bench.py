@@ -59,20 +59,25 @@ def _traffic(kernel: str):
 
 
 def _time_launches(fn, steps: int, warmup: int):
-    """Average milliseconds per call of fn() over `steps` calls, HIP events
-    on torch's current stream (the stream fn launches on)."""
+    """Milliseconds per call of fn() over `steps` back-to-back calls, from
+    HIP events on torch's current stream (the stream fn launches on): one
+    event before the first call and one after each, so the mean (whole
+    span / steps), median and minimum come from the same timed run."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = each[mid] if steps % 2 else 0.5 * (each[mid - 1] + each[mid])
+    return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": median,
+            "min": each[0]}
 
 
 def _bf16_workload(name):
@@ -92,10 +97,13 @@ def _cpu_baseline(w, host, budget_s: float):
     seeded inputs, as many as fit in the time budget."""
     import oracle
     import workloads
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()),
-                    default=1)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max((p.get("num_threads", 1) for p in pools), default=1)
+        if pools:
+            blas = f"{pools[0].get('internal_api')} {pools[0].get('version')}"
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     qh, kh, vh = host
@@ -120,6 +128,9 @@ def _cpu_baseline(w, host, budget_s: float):
         "sample": f"{n} of {w.B * w.H} heads of {w.name} (all {w.N} query "
                   f"rows of each head, fp64 numpy oracle, {secs:.1f} s); "
                   "same FLOP convention",
+        "wall_s": round(secs, 2),
+        "blas": blas,
+        "affinity_cores": len(os.sched_getaffinity(0)),
     }
 
 
@@ -152,6 +163,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     w, (q, k, v), host = _bf16_workload(workloads.HEADLINE)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
@@ -167,7 +179,8 @@ def main() -> int:
         del src, dst
 
     torch.cuda.synchronize()
-    ms = _time_launches(step, args.steps, args.warmup)
+    head = _time_launches(step, args.steps, args.warmup)
+    ms = head["mean"]
     tflops = w.flops / (ms * 1e-3) / 1e12
 
     extras = {}
@@ -178,10 +191,12 @@ def main() -> int:
             oo = torch.empty_like(qq)
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
-            m = _time_launches(lambda: fa.forward(qq, kk, vv, causal=ww.causal,
-                                                  out=oo, lse=ll), 20, 20)
+            tm = _time_launches(lambda: fa.forward(qq, kk, vv, causal=ww.causal,
+                                                   out=oo, lse=ll), 20, 20)
+            m = tm["mean"]
             t = ww.flops / (m * 1e-3) / 1e12
-            extras[name] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
+            extras[name] = {"ms": round(m, 4), "ms_median": round(tm["median"], 4),
+                            "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                             "frac_of_bf16_peak": round(t / BF16_PEAK_TFLOPS, 4)}
             del qq, kk, vv, oo, ll
         ww = workloads.WORKLOADS["fp8_n8192"]
@@ -198,13 +213,15 @@ def main() -> int:
                              device=dev)
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
-            m = _time_launches(lambda: fa.forward_fp8(q8, k8, v8, desc,
-                                                      out=oo, lse=ll), 20, 20)
+            tm = _time_launches(lambda: fa.forward_fp8(q8, k8, v8, desc,
+                                                       out=oo, lse=ll), 20, 20)
+            m = tm["mean"]
             t = ww.flops / (m * 1e-3) / 1e12
             key = "fp8_n8192" + ("_hadamard" if rot else "")
-            extras[key] = {"ms": round(m, 4), "TFLOP/s": round(t, 1),
+            extras[key] = {"ms": round(m, 4), "ms_median": round(tm["median"], 4),
+                           "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
-        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20)
+        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20)["mean"]
         nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
         extras["fp8_quantize_hadamard_per_tensor"] = {
             "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
@@ -218,7 +235,7 @@ def main() -> int:
         a = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
         bt = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
         c = torch.empty((8192, 8192), device=dev, dtype=torch.bfloat16)
-        mg = _time_launches(lambda: torch.matmul(a, bt, out=c), 20, 5)
+        mg = _time_launches(lambda: torch.matmul(a, bt, out=c), 20, 5)["mean"]
         tg = 2 * 8192 ** 3 / (mg * 1e-3) / 1e12
         extras["library_gemm_bf16_8192_randn"] = {
             "ms": round(mg, 4), "TFLOP/s": round(tg, 1),
@@ -228,6 +245,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu and rank == 0:
         cpu = _cpu_baseline(w, host, args.cpu_budget)
+        cpu["gpu_over_oracle"] = round(tflops / cpu["value"], 1)
 
     line = {
         "metric": METRIC,
@@ -237,6 +255,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(head["median"], 4),
+        "ms_min": round(head["min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -254,6 +274,7 @@ def main() -> int:
             "traffic": _traffic("fwd_bf16_d128"),
             "kernel": "fwd_bf16_kernel<128, false, 2>",
             "flops_per_launch": w.flops,
+            "peak_basis": f"{cus} CUs x 4096 bf16 FLOP/clk x 2.4 GHz",
         },
         "cpu_baseline": cpu,
         "extras": extras,

@@ -32,10 +32,11 @@
 //     integer (never decreasing) that keeps the tile's row maximum within
 //     log2(448/256) of it, and the P V MFMA takes the per-lane block scale
 //     2^E_t of the f8f6f4 instruction, so O accumulates p * 2^8 * 2^E_t
-//     relative to m0 exactly.  Two row sums follow it, each adding the
-//     tile's lane sum times 2^E_t: lq over the e4m3 values the product used
-//     (O = acc / lq, so a row whose weight sits on one key is not off by that
-//     key's rounding, up to 2^-4) and l over the fp32 p before rounding (the
+//     relative to m0 exactly.  Two row sums follow it: lq over the e4m3
+//     values the product used, from one more MFMA per tile with an all-ones
+//     A operand and the same block scale (O = acc / lq, so a row whose
+//     weight sits on one key is not off by that key's rounding, up to 2^-4),
+//     and l, the lanes' fp32 sums of p before rounding times 2^E_t (the
 //     LSE).  Both carry the same 2^8, which cancels in O and is removed from
 //     the LSE.  Only if E passes 64 (scores rising more than 64
 //     log2 units above block 0) are O and l renormalised, to keep fp32
@@ -101,20 +102,17 @@ __device__ __forceinline__ int pack_fp8x2(float a, float b, int old, int hi) {
             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
-// acc + the two e4m3 values in the low (hi = 0) or high (hi = 1) 16 bits of
-// w: decoded exactly to bf16, then a bf16 dot with (1, 1) into fp32.
-__device__ __forceinline__ float add_fp8x2(int w, int hi, float acc) {
-  const bf16x2_t x = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+// Maximum that propagates NaN (IEEE maximum): unlike fmaxf it needs no
+// quieting of its inputs, and three-input forms fold into v_maximum3_f32.
+__device__ __forceinline__ float maxf(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
 }
 
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
                                                   __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return maxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float half_sum(float x) {
@@ -282,7 +280,12 @@ fwd_fp8_kernel(const FwdArgs a) {
   float m0 = 0.f;                       // per-row base, log2 units
   int e_cur = 0;                        // E of the tile whose P is formed
   float l_run = 0.f;                    // this lane's half of sum p*2^8*2^E
-  float lq_run = 0.f;                   // same over the e4m3-rounded p*2^8
+  // Row sums of the e4m3 P the product used, times 2^E, from a fifth MFMA
+  // with an all-ones A: every row of the result is the column sum, so each
+  // lane's element 0 is the sum for its own query.
+  f32x16_t lacc = f32x16_t{};
+  const int ONE4 = 0x38383838;          // four e4m3 1.0
+  const i32x8_t ones = {ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4};
 
   // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
   auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
@@ -308,12 +311,12 @@ fwd_fp8_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = 4 * i;
-      m[i] = fmaxf(fmaxf(s[j >> 4][j & 15], s[(j + 1) >> 4][(j + 1) & 15]),
-                   fmaxf(s[(j + 2) >> 4][(j + 2) & 15],
-                         s[(j + 3) >> 4][(j + 3) & 15]));
+      m[i] = maxf(maxf(s[j >> 4][j & 15], s[(j + 1) >> 4][(j + 1) & 15]),
+                  maxf(s[(j + 2) >> 4][(j + 2) & 15],
+                       s[(j + 3) >> 4][(j + 3) & 15]));
     }
-    const float mx = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])),
-                           fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+    const float mx = maxf(maxf(maxf(m[0], m[1]), maxf(m[2], m[3])),
+                          maxf(maxf(m[4], m[5]), maxf(m[6], m[7])));
     return half_max(mx);
   };
   // E for a tile with row maximum mx (raw score): the smallest integer,
@@ -355,7 +358,7 @@ fwd_fp8_kernel(const FwdArgs a) {
     int pw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) pw[i] = 0;
-    float ls0 = 0.f, ls1 = 0.f, lq0 = 0.f, lq1 = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -386,21 +389,15 @@ fwd_fp8_kernel(const FwdArgs a) {
         const int pr = 4 * i + q;
         pw[pr >> 1] = pack_fp8x2(e[q][0], e[q][1], pw[pr >> 1], pr & 1);
         if (q & 1) ls1 += e[q][0] + e[q][1]; else ls0 += e[q][0] + e[q][1];
-      }
-      // l sums the rounded values the P V product uses, so a row whose
-      // weight sits on one key still divides that key's value by itself.
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int pr = 4 * i + q;
-        if (q & 1) lq1 = add_fp8x2(pw[pr >> 1], pr & 1, lq1);
-        else lq0 = add_fp8x2(pw[pr >> 1], pr & 1, lq0);
-        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1), "+v"(lq0),
-                     "+v"(lq1));
+        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // O is divided by the sum of the rounded values the P V product used,
+    // so a row whose weight sits on one key still divides that key's value
+    // by itself; l (fp32 p before rounding) gives the LSE.
+    if constexpr (PV) lacc = mfma_f8_bscale(ones, pp, lacc, eb);
     l_run += __builtin_ldexpf(ls0 + ls1, e_cur);
-    lq_run += __builtin_ldexpf(lq0 + lq1, e_cur);
     pp = i32x8_t{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     e_pp = e_cur;
     if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BT);
@@ -416,7 +413,8 @@ fwd_fp8_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
       l_run *= f;
-      lq_run *= f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lacc[r] *= f;
       m0 += static_cast<float>(sh);
       e_pp = max(e_pp - sh, -127);
       e_cur = 0;
@@ -456,7 +454,7 @@ fwd_fp8_kernel(const FwdArgs a) {
   // O divides by the sum of the weights it was built from (the e4m3 values);
   // the LSE takes the sum of the unrounded p.
   const float l_tot = half_sum(l_run);
-  const float lq_tot = half_sum(lq_run);
+  const float lq_tot = lacc[0];
   const float inv = (lq_tot > 0.f) ? dv / lq_tot : 0.f;
   if (qrow < N) {
     uint16_t* op = static_cast<uint16_t*>(a.o) +
