@@ -15,11 +15,13 @@
 //     exactly its 32-byte B operand of the P V product (K rows in sigma
 //     order, fa_common.h), and the V^T operand comes from the transposing
 //     ds_read_b64_tr_b8.
-//   * Workgroup = 8 waves of 32 query rows (BR = 256), two waves per SIMD:
-//     with fp8 the matrix work per score halves, so the vector work of the
-//     softmax needs the issue slots of two waves.  K and V tiles of 64 keys
-//     go from HBM/L2 straight into LDS with buffer_load_dwordx4 ... lds (one
-//     1 KB window of each per wave), double-buffered.
+//   * Workgroup = 4 waves of 32 query rows (BR = 128), two workgroups per
+//     CU, so two waves per SIMD: with fp8 the matrix work per score halves,
+//     so the vector work of the softmax needs the issue slots of two waves,
+//     and waves of different workgroups never wait at each other's barrier.
+//     K and V tiles of 64 keys go from HBM/L2 straight into LDS with
+//     buffer_load_dwordx4 ... lds (two 1 KB windows of each per wave),
+//     double-buffered.
 //   * A three-stage software pipeline runs in every step t: one issue slot
 //     per MFMA pair, the scores MFMA of tile t+1, p = exp2(S c - m + 8) for
 //     four score pairs of tile t, the P V MFMA of tile t-1, then the e4m3
@@ -48,10 +50,10 @@ namespace fa {
 namespace {
 
 constexpr int D = 128;
-constexpr int NWAVE = 8;
-constexpr int BR = 32 * NWAVE;       // query rows per workgroup
 constexpr int BT = 64;               // keys per tile (= per step)
-constexpr int NTHR = 64 * NWAVE;
+// Waves per workgroup.  Two workgroups share a CU (registers and LDS allow
+// it), so each SIMD runs two waves that never wait on each other's barrier.
+constexpr int NWAVE_FP8 = 4;
 constexpr int NCH = D / 16;          // 16-byte chunks per row (8)
 constexpr float P_SHIFT = 8.0f;      // P is stored as p * 2^8
 // p * 2^8 <= 448 (largest finite e4m3) when the score is at most
@@ -149,9 +151,17 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
       0);
 }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(NTHR, 1)
+template <bool CAUSAL, int NWAVE>
+__global__ void __launch_bounds__(64 * NWAVE, 1)
 fwd_fp8_kernel(const FwdArgs a) {
+  constexpr int BR = 32 * NWAVE;               // query rows per workgroup
+  // 1 KB copy windows per tile and operand, and how many each wave issues.
+  constexpr int NWIN = BT * NCH / (64 * NWAVE);
+  static_assert(NWIN * 64 * NWAVE == BT * NCH, "whole windows per wave");
+  // Window w of wave v covers rows 8 (v + NWAVE w) .. +7: a multiple of 32
+  // rows apart, so the swizzles (which depend on the row mod 32) repeat.
+  static_assert(NWIN == 1 || (8 * NWAVE) % 32 == 0, "window spacing");
+  constexpr uint32_t WIN_BYTES = 8 * NWAVE * D;  // global offset per window
   __shared__ uint4 Ks0[BT * NCH];
   __shared__ uint4 Ks1[BT * NCH];
   __shared__ uint4 Vs0[BT * NCH];
@@ -222,7 +232,6 @@ fwd_fp8_kernel(const FwdArgs a) {
     koff = static_cast<uint32_t>(r * D + 16 * kswz(r, p));
     voff = static_cast<uint32_t>(r * D + 16 * vswz(r, p));
   }
-  static_assert(BT * NCH == 64 * NWAVE, "one copy window per wave");
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
   const int ntiles = (kv_end + BT - 1) / BT;
@@ -365,8 +374,15 @@ fwd_fp8_kernel(const FwdArgs a) {
       const i32x8_t kcur = kf;
       if (i + 1 < 4) kf = kfrag(kr, (i + 1) & 1, (i + 1) >> 1);
       sn[i & 1] = mfma_f8(kcur, qf[i >> 1], sn[i & 1]);
-      if (i == 0) copy_to_lds(rv, vw + 64 * wave, voff);
-      if (i == 1) copy_to_lds(rk, kw + 64 * wave, koff);
+      // Copies spread over the slots: V window i / 2 on even slots, K window
+      // i / 2 on odd ones.
+      if (i / 2 < NWIN) {
+        const int w = i / 2;
+        if (i % 2 == 0)
+          copy_to_lds(rv, vw + 64 * (wave + NWAVE * w), voff + w * WIN_BYTES);
+        else
+          copy_to_lds(rk, kw + 64 * (wave + NWAVE * w), koff + w * WIN_BYTES);
+      }
       __builtin_amdgcn_sched_barrier(0);
       float e[4][2];
 #pragma unroll
@@ -382,6 +398,9 @@ fwd_fp8_kernel(const FwdArgs a) {
         const i32x8_t vcur = vf;
         if (i + 1 < 4) vf = vfrag(vr, i + 1);
         oacc[i] = mfma_f8_bscale(vcur, pp, oacc[i], eb);
+        // Keeps the product in its slot: without a use here the compiler
+        // sinks all four past the masking branch, after the exps.
+        asm volatile("" : "+v"(oacc[i]));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -424,8 +443,13 @@ fwd_fp8_kernel(const FwdArgs a) {
   // ---- prologue: K tiles 0 and 1 into LDS, scores of tile 0 ----
   // Stages: tile u lives in Ks[u % 2] / Vs[u % 2]; step t reads K(t+1) and
   // V(t-1), both from stage (t+1) % 2, and fills stage t % 2.
-  copy_to_lds(rsrc_at(kp, 0), Ks0 + 64 * wave, koff);
-  copy_to_lds(rsrc_at(kp, BT), Ks1 + 64 * wave, koff);
+#pragma unroll
+  for (int w = 0; w < NWIN; ++w) {
+    copy_to_lds(rsrc_at(kp, 0), Ks0 + 64 * (wave + NWAVE * w),
+                koff + w * WIN_BYTES);
+    copy_to_lds(rsrc_at(kp, BT), Ks1 + 64 * (wave + NWAVE * w),
+                koff + w * WIN_BYTES);
+  }
   wait_copies_and_sync();
   f32x16_t s[2];
   s[0] = f32x16_t{};
@@ -480,7 +504,9 @@ fwd_fp8_kernel(const FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
+template <int NWAVE>
+hipError_t launch_waves(FwdArgs a, bool causal, hipStream_t stream) {
+  constexpr int BR = 32 * NWAVE;
   a.nqb = (a.N + BR - 1) / BR;
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
@@ -491,13 +517,17 @@ hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
   if (causal) {
-    hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3((int)grid), dim3(NTHR), 0,
-                       stream, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<true, NWAVE>), dim3((int)grid),
+                       dim3(64 * NWAVE), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3((int)grid), dim3(NTHR), 0,
-                       stream, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<false, NWAVE>), dim3((int)grid),
+                       dim3(64 * NWAVE), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
+  return launch_waves<NWAVE_FP8>(a, causal, stream);
 }
 
 }  // namespace fa
