@@ -291,6 +291,11 @@ fwd_bf16_kernel(const FwdArgs a) {
   constexpr uint32_t VSTRIDE = (64 * NWAVE / G::NCH) * D * 2;
   static_assert(VSTRIDE == 1024 * NWAVE, "V copy stride");
   const int kinst = (G::KINS - wave + NWAVE - 1) / NWAVE;   // K copies issued
+  // Every wave issues at least KINS / NWAVE of them: stated so that those
+  // copies need no branch.
+  auto has_k_copy = [&](int i) {
+    return i < G::KINS / NWAVE || i < kinst;
+  };
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
   const int ntiles = (kv_end + BT - 1) / BT;
@@ -313,7 +318,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     const auto rs = rsrc_at(kp, tile * BT);
 #pragma unroll
     for (int i = 0; i < G::KPW; ++i)
-      if (i < kinst)
+      if (has_k_copy(i))
         copy_to_lds(rs, stage + 64 * (wave + NWAVE * i),
                     i < KREG ? (koff2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu
                              : k_offset(i));
@@ -334,7 +339,7 @@ fwd_bf16_kernel(const FwdArgs a) {
       copy_to_lds(rv, vw + 64 * (wave + NWAVE * n), voff0, VSTRIDE * n);
     } else {
       const int i = n - G::VPW;
-      if (i < kinst)
+      if (has_k_copy(i))
         copy_to_lds(rk, kw + 64 * (wave + NWAVE * i),
                     i < KREG ? (koff2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu
                              : k_offset(i));
