@@ -12,6 +12,11 @@ Everything here is plain, slow and written to be read against the pages:
   pass).  This is the "classic" computation that the FlashAttention v1 post
   (DeepSchool #630), sections «Проблема базового attention» and
   «Онлайн-Softmax», says the tiled method reproduces exactly.
+* ``attention_bwd`` -- the exact gradients dQ, dK, dV of the same
+  definition for a given dO, with the softmax recomputed (the pages name
+  recomputation, FlashAttention-3 summary, «Resumo do FlashAttention», and
+  the backward pass's shared-memory bottleneck, FlashAttention-4 page,
+  paragraph 2, but give no formulas).
 * ``fp8``        -- OCP e4m3 ("e4m3fn") encode/decode from the format's
   definition and per-tensor quantisation, for the low-precision path of the
   FlashAttention-3 summary (GeekNews), section «Novos recursos de hardware
@@ -25,6 +30,10 @@ Parity status of each function is stated in its module header.
 """
 
 from .attention import attention, attention_rows  # noqa: F401
+from .attention_bwd import (  # noqa: F401
+    attention_backward,
+    attention_backward_sampled,
+)
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,
