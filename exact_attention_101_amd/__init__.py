@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -58,6 +58,9 @@ def library() -> ctypes.CDLL:
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                    i32, i32, f32, vp, vp]
         lib.fa_fwd_fp8.restype = i32
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                               i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_bwd.restype = i32
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i64, i32, vp, vp]
         lib.fa_fp8_quantize.restype = i32
         lib.fa_status_string.argtypes = [i32]
@@ -120,6 +123,46 @@ def forward(q, k, v, *, causal: bool = False, scale=None, out=None,
         lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
         FA_DTYPE_BF16, _stream_handle(q.device)))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale=None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """bf16 attention backward (d = 128): gradients of the forward that
+    produced o and lse, for the output gradient dout.  Returns (dq, dk, dv),
+    bfloat16, shaped like q, k, v.  workspace: optional float32 tensor of
+    2 * B * H * N elements (allocated if None)."""
+    import torch
+    B, H, Hkv, N, d = _shape_check(q, k, v)
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("backward expects bfloat16 q, k, v, o, dout")
+    for t in (o, dout):
+        if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("o and dout must be contiguous and shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or \
+            not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(2 * B * H * N, dtype=torch.float32,
+                                device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * N \
+            or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous float32 tensor of "
+                         "at least 2 * B * H * N elements")
+    _check(library().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), workspace.data_ptr(), B, H, Hkv, N, d,
+        int(bool(causal)), float(scale), _stream_handle(q.device)))
+    return dq, dk, dv
 
 
 def forward_fp8(q8, k8, v8, descale_qkv=None, *, causal: bool = False,

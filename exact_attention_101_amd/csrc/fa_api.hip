@@ -12,6 +12,7 @@
 namespace fa {
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
                                long long rows, uint64_t sign_lo,
                                uint64_t sign_hi, bool rotate,
@@ -106,6 +107,41 @@ FA_EXPORT int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
   a.descale = descale_qkv;
   return hip_status(
       fa::launch_fwd_fp8(a, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, float* workspace, int B,
+                     int H, int Hkv, int N, int d, int causal, float scale,
+                     void* stream) {
+  if (!o || !dout || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARGUMENT;
+  const int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale,
+                           d == 128);
+  if (st != FA_OK) return st;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = workspace;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.group = H / Hkv;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  return hip_status(
+      fa::launch_bwd_bf16(a, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,

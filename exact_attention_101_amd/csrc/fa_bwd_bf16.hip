@@ -1,0 +1,489 @@
+// Attention backward (bf16 in and out, fp32 accumulation) for gfx950
+// (MI355X), d = 128.
+//
+// The pages give the backward pass only in outline: FlashAttention keeps the
+// softmax matrix off HBM by recomputing it (FlashAttention-3 summary,
+// GeekNews, section «Resumo do FlashAttention»), and the backward pass is
+// bound by on-chip shared-memory traffic rather than the matrix units
+// (FlashAttention-4 page, smntcn.com, paragraph 2).  The gradients are those
+// of O = softmax(scale Q K^T [+ causal mask]) V for a given dO:
+//     P = exp(scale Q K^T - LSE)     (recomputed from the forward's LSE)
+//     dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D)
+//     dQ = scale dS K,  dK = scale dS^T Q
+//
+// Three launches, no atomics, deterministic:
+//   * bwd_prep_kernel: ws[i] = {LSE_i log2(e), D_i} for every query row.
+//   * bwd_dq_kernel: one lane per query, as in the forward kernel; 32-key
+//     tiles of K and V stream through LDS.  S^T = K Q^T and dP^T = V dO^T on
+//     MFMA (K and V rows in the forward's sigma order, Q^T and dO^T held as
+//     B operands in registers), dS^T in the layout of the forward's P, and
+//     dQ^T += K^T dS^T with K^T read by the transposing LDS read, exactly
+//     the forward's O^T += V^T P^T.
+//   * bwd_dkdv_kernel: one lane per key; 32-query tiles of Q and dO (and
+//     their ws entries) stream through LDS for every query head of the KV
+//     head's group.  S = Q K^T and dP = dO V^T with K^T and V^T held in
+//     registers, then dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T
+//     from transposing reads.
+//
+// LDS layouts of a 32-row tile (rows are keys or queries, 16-byte chunks):
+//   row layout: row r at chunks r * 17 .. r * 17 + 15 (one pad chunk per row)
+//     for the row fragments, read in sigma order;
+//   transposed-read layout: row r, chunk c stored at chunk
+//     r * 16 + ((c / 4) ^ (r % 4)) * 4 + c % 4, for ds_read_b64_tr_b16.
+// Tiles arrive by buffer_load_dwordx4 ... lds; rows past N read zeros.
+#include "fa_common.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int NCH = D / 8;                  // 16-byte chunks per row
+constexpr int KSL = NCH + 1;                // padded row stride, chunks
+constexpr int T = 32;                       // rows per tile (one step)
+constexpr int NW = 4;                       // waves per workgroup
+constexpr int NTHR = 64 * NW;
+constexpr int BLK = T * NW;                 // rows per workgroup (128)
+constexpr int ROW_SLOTS = T * KSL;          // 544
+constexpr int ROW_COPIES = (ROW_SLOTS + 63) / 64;   // 9 (the last partly pad)
+constexpr int ROW_ALLOC = ROW_COPIES * 64;  // 576 chunks
+constexpr int TR_SLOTS = T * NCH;           // 512
+constexpr int TR_COPIES = TR_SLOTS / 64;    // 8
+constexpr int ROW_PW = (ROW_COPIES + NW - 1) / NW;  // 3 (wave 0), others 2
+constexpr int TR_PW = TR_COPIES / NW;               // 2
+constexpr uint32_t FAR = 0x80000000u;       // past any descriptor: reads 0
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b,
+                                         const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 64-lane copy of 16 (copy16) or 4 (copy4) bytes per lane from `rsrc`
+// + voffset into LDS at `dst` + that many bytes * lane.  Offsets past the
+// descriptor's size read 0.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc,
+                                       const void* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset, 0, 0,
+      0);
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc,
+                                      const void* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 4, voffset, 0, 0,
+      0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base,
+                                                            int64_t row0,
+                                                            int rows,
+                                                            int row_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(base) + row0 * row_bytes), 0,
+      max(rows, 0) * row_bytes, 0x00020000);
+}
+
+// Per-lane global byte offsets of the copies one wave issues for a 32-row
+// tile of 256-byte rows: row layout (copies wave, wave + 4, wave + 8) and
+// transposed-read layout (copies wave, wave + 4).
+struct TileCopy {
+  uint32_t row_off[ROW_PW];
+  uint32_t tr_off[TR_PW];
+  int nrow;                                  // row-layout copies of this wave
+
+  __device__ void init(int wave, int lane) {
+    nrow = 0;
+#pragma unroll
+    for (int i = 0; i < ROW_PW; ++i) {
+      const int j = wave + NW * i;
+      const int slot = 64 * j + lane;
+      const int r = slot / KSL, c = slot % KSL;
+      row_off[i] = (j < ROW_COPIES && r < T && c < NCH)
+                       ? static_cast<uint32_t>(r * D * 2 + c * 16)
+                       : FAR;
+      if (j < ROW_COPIES) nrow = i + 1;
+    }
+#pragma unroll
+    for (int i = 0; i < TR_PW; ++i) {
+      const int slot = 64 * (wave + NW * i) + lane;
+      const int r = slot / NCH, p = slot % NCH;
+      const int c = (((p >> 2) ^ (r & 3)) << 2) | (p & 3);
+      tr_off[i] = static_cast<uint32_t>(r * D * 2 + c * 16);
+    }
+  }
+
+  __device__ void rows(__amdgpu_buffer_rsrc_t rs, const uint4* dst,
+                       int wave) const {
+#pragma unroll
+    for (int i = 0; i < ROW_PW; ++i)
+      if (i < ROW_COPIES / NW || i < nrow)
+        copy16(rs, dst + 64 * (wave + NW * i), row_off[i]);
+  }
+  __device__ void tr(__amdgpu_buffer_rsrc_t rs, const uint4* dst,
+                     int wave) const {
+#pragma unroll
+    for (int i = 0; i < TR_PW; ++i)
+      copy16(rs, dst + 64 * (wave + NW * i), tr_off[i]);
+  }
+};
+
+// Byte offset, inside a transposed-read tile, of lane's first 8-byte read
+// for d block 0 (see the forward kernel's V reads): lane 16 g + 4 R + j
+// reads row 8 h + R at d = 16 (g % 2) + 8 (j % 2) + 4 (j / 2), and the
+// output lane then holds 4 rows of d = 32 db + sigma(lane % 32).
+__device__ __forceinline__ int tr_base(int lane) {
+  const int h = lane >> 5;
+  const int R = (lane >> 2) & 3;
+  const int j = lane & 3;
+  const int r = 8 * h + R;
+  const int ch = 4 * (r & 3) + 2 * ((lane >> 4) & 1) + (j & 1);
+  return (r * NCH + ch) * 16 + 8 * (j >> 1);
+}
+
+// A operand X^T (rows d = 32 db + sigma(m), k = rows 16 u .. 16 u + 15 of
+// the tile) from a transposed-read tile.
+__device__ __forceinline__ bf16x8_t tr_frag(const uint4* tile, int base,
+                                            int db, int u) {
+  const char* p = reinterpret_cast<const char*>(tile) + (base ^ (db << 6)) +
+                  16 * u * NCH * 16;
+  const i16x4_t x0 = lds_read_tr16(p);
+  const i16x4_t x1 = lds_read_tr16(p + 4 * NCH * 16);
+  return __builtin_bit_cast(
+      bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand from a row-layout tile: row sigma(li) of the tile, d chunk
+// 8 h + s (k-step s covers d = 8 s .. 8 s + 7 and 64 + 8 s .. 64 + 8 s + 7).
+__device__ __forceinline__ bf16x8_t row_frag(const uint4* tile, int li, int h,
+                                             int s) {
+  return as_bf16x8(tile[sigma(li) * KSL + 8 * h + s]);
+}
+
+// B-operand register fragments of one 128-wide row (query or key) for the
+// eight k-steps: lane half h, step s holds d = 64 h + 8 s .. + 7.
+__device__ __forceinline__ void load_row_b(const uint16_t* base, int row,
+                                           int N, int h, bf16x8_t (&f)[8]) {
+  const bool ok = row < N;
+  const uint4* src = reinterpret_cast<const uint4*>(
+      base + static_cast<int64_t>(ok ? row : 0) * D + 64 * h);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f[s] = as_bf16x8(keep_if(src[s], ok));
+}
+
+// Store 32 rows x 128 of an O^T-shaped accumulator (row m <-> d = 32 db +
+// sigma(m)): lane half h holds d = 32 db + 16 u + 8 h .. + 7 in registers
+// 8 u .. 8 u + 7, for the lane's row.
+__device__ __forceinline__ void store_rows(uint16_t* dst,
+                                           const f32x16_t (&acc)[4],
+                                           float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x16_t& o = acc[db];
+      uint4 w;
+      w.x = pack_bf16x2(o[8 * u + 0] * mul, o[8 * u + 1] * mul);
+      w.y = pack_bf16x2(o[8 * u + 2] * mul, o[8 * u + 3] * mul);
+      w.z = pack_bf16x2(o[8 * u + 4] * mul, o[8 * u + 5] * mul);
+      w.w = pack_bf16x2(o[8 * u + 6] * mul, o[8 * u + 7] * mul);
+      *reinterpret_cast<uint4*>(dst + 32 * db + 16 * u + 8 * h) = w;
+    }
+  }
+}
+
+// Pack 16 fp32 values of an S-shaped accumulator (register r <-> tile row
+// 16 (r / 8) + 8 h + r % 8) into the two bf16 B operands of k-steps 0, 1.
+__device__ __forceinline__ void pack_b(const float (&x)[16],
+                                       bf16x8_t (&b)[2]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    uint4 w;
+    w.x = pack_bf16x2(x[8 * u + 0], x[8 * u + 1]);
+    w.y = pack_bf16x2(x[8 * u + 2], x[8 * u + 3]);
+    w.z = pack_bf16x2(x[8 * u + 4], x[8 * u + 5]);
+    w.w = pack_bf16x2(x[8 * u + 6], x[8 * u + 7]);
+    b[u] = as_bf16x8(w);
+  }
+}
+
+// ---- ws[i] = {LSE_i log2(e), dO_i . O_i}: 16 lanes per row ----
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdArgs a,
+                                                       long long rows) {
+  const long long row = static_cast<long long>(blockIdx.x) * 16 +
+                        (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 x = reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(a.o) + row * D)[c];
+    const uint4 y = reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(a.dout) + row * D)[c];
+    const bf16x8_t xo = as_bf16x8(x), yo = as_bf16x8(y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = fmaf(static_cast<float>(xo[i]), static_cast<float>(yo[i]), acc);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (row < rows && c == 0) {
+    a.ws[2 * row] = a.lse[row] * LOG2E;
+    a.ws[2 * row + 1] = acc;
+  }
+}
+
+// ---- dQ: one lane per query ----
+template <bool CAUSAL>
+__global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
+  __shared__ uint4 Kr[2][ROW_ALLOC];
+  __shared__ uint4 Kt[2][TR_SLOTS];
+  __shared__ uint4 Vr[2][ROW_ALLOC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int h = lane >> 5;
+
+  int bh, qb;
+  map_work(blockIdx.x, gridDim.x, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh,
+           qb);
+  const int b = bh / a.H;
+  const int hq = bh % a.H;
+  const int hk = hq / a.group;
+  const int N = a.N;
+  const int q0 = qb * BLK;
+  const int qw0 = q0 + T * wave;
+  const int qrow = qw0 + li;
+
+  const int64_t qhead = (static_cast<int64_t>(b) * a.H + hq) * N;
+  const int64_t khead = (static_cast<int64_t>(b) * a.Hkv + hk) * N;
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + khead * D;
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + khead * D;
+
+  bf16x8_t qf[8], of[8];
+  load_row_b(static_cast<const uint16_t*>(a.q) + qhead * D, qrow, N, h, qf);
+  load_row_b(static_cast<const uint16_t*>(a.dout) + qhead * D, qrow, N, h,
+             of);
+  const bool qok = qrow < N;
+  const float lse2 = qok ? a.ws[2 * (qhead + qrow)] : 0.f;
+  const float dq_row = qok ? a.ws[2 * (qhead + qrow) + 1] : 0.f;
+
+  TileCopy cp;
+  cp.init(wave, lane);
+  const int trb = tr_base(lane);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BLK) : N;
+  const int ntiles = (kv_end + T - 1) / T;
+  auto issue = [&](int t, int st) {
+    const int r0 = t * T;
+    const auto rk = rows_rsrc(kp, r0, kv_end - r0, D * 2);
+    const auto rv = rows_rsrc(vp, r0, kv_end - r0, D * 2);
+    cp.rows(rk, Kr[st], wave);
+    cp.tr(rk, Kt[st], wave);
+    cp.rows(rv, Vr[st], wave);
+  };
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+
+  issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile has landed
+    __syncthreads();                      // and every wave is done with st^1
+    if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+    const int k0 = t * T;
+    if (CAUSAL && k0 > qw0 + T - 1) continue;   // wave's rows see no key
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int f = 0; f < 8; ++f) s = mfma(row_frag(Kr[st], li, h, f), qf[f], s);
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      dp = mfma(row_frag(Vr[st], li, h, f), of[f], dp);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
+      const bool ok = qok && key < N && (!CAUSAL || key <= qrow);
+      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -lse2))
+                         : 0.f;
+      ds[r] = p * (dp[r] - dq_row);
+    }
+    bf16x8_t dsb[2];
+    pack_b(ds, dsb);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[db] = mfma(tr_frag(Kt[st], trb, db, u), dsb[u], acc[db]);
+  }
+
+  if (qok) {
+    uint16_t* dst =
+        static_cast<uint16_t*>(a.dq) + (qhead + qrow) * static_cast<int64_t>(D);
+    store_rows(dst, acc, a.scale, h);
+  }
+}
+
+// ---- dK, dV: one lane per key ----
+template <bool CAUSAL>
+__global__ void __launch_bounds__(NTHR, 1) bwd_dkdv_kernel(const BwdArgs a) {
+  __shared__ uint4 Qr[2][ROW_ALLOC];
+  __shared__ uint4 Qt[2][TR_SLOTS];
+  __shared__ uint4 Or[2][ROW_ALLOC];     // dO, row layout
+  __shared__ uint4 Ot[2][TR_SLOTS];      // dO, transposed-read layout
+  __shared__ float Ws[2][2 * T];         // {LSE log2(e), D} of the tile rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int h = lane >> 5;
+
+  const int unit = blockIdx.x;
+  const int bhk = unit / a.nkb;
+  const int kb = a.nkb - 1 - unit % a.nkb;    // causal: longest first
+  const int b = bhk / a.Hkv;
+  const int hk = bhk % a.Hkv;
+  const int N = a.N;
+  const int k0 = kb * BLK;
+  const int kw0 = k0 + T * wave;
+  const int key = kw0 + li;
+  const bool kok = key < N;
+
+  const int64_t khead = (static_cast<int64_t>(b) * a.Hkv + hk) * N;
+  bf16x8_t kf[8], vf[8];
+  load_row_b(static_cast<const uint16_t*>(a.k) + khead * D, key, N, h, kf);
+  load_row_b(static_cast<const uint16_t*>(a.v) + khead * D, key, N, h, vf);
+
+  TileCopy cp;
+  cp.init(wave, lane);
+  const int trb = tr_base(lane);
+
+  // Query tiles: every query head of the group, from the first tile that
+  // holds a query >= k0 (causal) or 0.
+  const int t0 = CAUSAL ? k0 / T : 0;
+  const int ntq = (N + T - 1) / T;
+  const int per_head = ntq - t0;
+  const int nsteps = per_head * a.group;
+  auto issue = [&](int step, int st) {
+    const int hq = hk * a.group + step / per_head;
+    const int t = t0 + step % per_head;
+    const int64_t qhead = (static_cast<int64_t>(b) * a.H + hq) * N;
+    const int r0 = t * T;
+    const auto rq = rows_rsrc(static_cast<const uint16_t*>(a.q) + qhead * D,
+                              r0, N - r0, D * 2);
+    const auto ro = rows_rsrc(static_cast<const uint16_t*>(a.dout) + qhead * D,
+                              r0, N - r0, D * 2);
+    cp.rows(rq, Qr[st], wave);
+    cp.tr(rq, Qt[st], wave);
+    cp.rows(ro, Or[st], wave);
+    cp.tr(ro, Ot[st], wave);
+    if (wave == 0) {
+      const auto rw = rows_rsrc(a.ws + 2 * qhead, r0, N - r0, 8);
+      copy4(rw, Ws[st], 4u * lane);
+    }
+  };
+
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dk[i] = f32x16_t{};
+    dv[i] = f32x16_t{};
+  }
+
+  if (nsteps > 0) issue(0, 0);
+  for (int step = 0; step < nsteps; ++step) {
+    const int st = step & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (step + 1 < nsteps) issue(step + 1, st ^ 1);
+    const int qt0 = (t0 + step % per_head) * T;
+    if (CAUSAL && qt0 + T - 1 < kw0) continue;   // no query sees these keys
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int f = 0; f < 8; ++f) s = mfma(row_frag(Qr[st], li, h, f), kf[f], s);
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      dp = mfma(row_frag(Or[st], li, h, f), vf[f], dp);
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 16 * (r >> 3) + 8 * h + (r & 7);   // row in the tile
+      const int q = qt0 + qi;
+      const float2 w = *reinterpret_cast<const float2*>(&Ws[st][2 * qi]);
+      const bool ok = kok && q < N && (!CAUSAL || key <= q);
+      p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -w.x)) : 0.f;
+      ds[r] = p[r] * (dp[r] - w.y);
+    }
+    bf16x8_t pb[2], dsb[2];
+    pack_b(p, pb);
+    pack_b(ds, dsb);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        dv[db] = mfma(tr_frag(Ot[st], trb, db, u), pb[u], dv[db]);
+        dk[db] = mfma(tr_frag(Qt[st], trb, db, u), dsb[u], dk[db]);
+      }
+  }
+
+  if (kok) {
+    const int64_t off = (khead + key) * static_cast<int64_t>(D);
+    store_rows(static_cast<uint16_t*>(a.dk) + off, dk, a.scale, h);
+    store_rows(static_cast<uint16_t*>(a.dv) + off, dv, 1.f, h);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream) {
+  const long long rows = static_cast<long long>(a.B) * a.H * a.N;
+  const long long prep_grid = (rows + 15) / 16;
+  a.nqb = (a.N + BLK - 1) / BLK;
+  a.nkb = (a.N + BLK - 1) / BLK;
+  const long long dq_grid = static_cast<long long>(a.B) * a.H * a.nqb;
+  const long long kv_grid = static_cast<long long>(a.B) * a.Hkv * a.nkb;
+  if (prep_grid > 0x7FFFFFFFLL || dq_grid > 0x7FFFFFFFLL ||
+      kv_grid > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
+  // Per-head byte ranges are addressed by 32-bit buffer offsets.
+  if (static_cast<long long>(a.N) * D * 2 > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
+  const int bh = a.B * a.H;
+  a.xcd_chunk = causal ? (bh % 8 == 0) : (dq_grid % 8 == 0);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((int)prep_grid), dim3(256), 0,
+                     stream, a, rows);
+  if (causal) {
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((int)dq_grid), dim3(NTHR), 0,
+                       stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((int)kv_grid), dim3(NTHR),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((int)dq_grid), dim3(NTHR),
+                       0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((int)kv_grid),
+                       dim3(NTHR), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

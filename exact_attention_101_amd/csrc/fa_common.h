@@ -30,6 +30,29 @@ struct FwdArgs {
   int xcd_chunk;          // 1: map workgroups to XCD-contiguous work ranges
 };
 
+// Arguments of one backward pass (bf16, d = 128).  ws holds, per query row
+// (b, h, i), the pair {LSE_i * log2(e), D_i = dO_i . O_i}, written by the
+// preprocessing kernel and read by both gradient kernels.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;              // [B, H, N, 2]
+  int B, H, Hkv, N;
+  int group;              // H / Hkv
+  int nqb;                // query blocks (dQ kernel)
+  int nkb;                // key blocks (dK / dV kernel)
+  float c;                // scale * log2(e), signed
+  float scale;            // signed
+  int xcd_chunk;          // as in FwdArgs, for the dQ kernel's grid
+};
+
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).
 __device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {

@@ -100,6 +100,36 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o,
                float scale, const float* descale_qkv, void* stream);
 
 /*
+ * fa_bwd -- gradients of the bf16 forward: dQ, dK, dV for a given dO.
+ *   The pages name recomputation as the way FlashAttention avoids storing
+ *   the attention matrix (FlashAttention-3 summary, GeekNews, section
+ *   «Resumo do FlashAttention») and shared-memory traffic as the backward
+ *   pass's bottleneck (FlashAttention-4 page, smntcn.com, paragraph 2); the
+ *   formulas are the exact gradients of the forward's definition, with the
+ *   softmax recomputed from the forward's LSE:
+ *       P = exp(scale Q K^T - LSE), dV = P^T dO, dP = dO V^T,
+ *       D_i = dO_i . O_i, dS = P * (dP - D), dQ = scale dS K,
+ *       dK = scale dS^T Q; with GQA, dK and dV sum over each KV head's
+ *       query heads.
+ *   q, k, v, o, lse   the forward's inputs and outputs (read only): bf16
+ *                     [B][H][N][d] / [B][Hkv][N][d], lse float [B][H][N].
+ *   dout      device, bfloat16 [B][H][N][d] (read only): dL/dO.
+ *   dq        device, bfloat16 [B][H][N][d] (written).
+ *   dk, dv    device, bfloat16 [B][Hkv][N][d] (written).
+ *   workspace device, float [B][H][N][2], caller-owned scratch (written):
+ *             {LSE * log2(e), D} per query row.  Not an output.
+ *   d         must be 128.  B, H, Hkv, N, causal, scale as for fa_fwd.
+ *   stream    hipStream_t or NULL; three kernels are enqueued on it.
+ *   Errors as for fa_fwd; a null dout, dq, dk, dv or workspace is
+ *   FA_ERR_INVALID_ARGUMENT, a misaligned one FA_ERR_MISALIGNED.
+ *   Deterministic: no atomics, the same inputs give the same bits.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           float* workspace, int B, int H, int Hkv, int N, int d, int causal,
+           float scale, void* stream);
+
+/*
  * fa_fp8_quantize -- optional random-sign Hadamard rotation of each row, then
  * per-tensor OCP e4m3 quantisation ("incoherent processing" of the
  * FlashAttention-3 summary, section «Baixa precisão: redução do erro de

@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ("fa_fwd", "fa_fwd_fp8", "fa_fp8_quantize", "fa_status_string",
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fp8_quantize",
+              "fa_status_string",
               "fa_last_hip_error", "fa_version"):
         assert n in names
 
@@ -107,3 +108,26 @@ def test_python_wrapper_raises_without_gpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(x, x, x)
+
+
+def _bwd(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A, B=1,
+         H=2, Hkv=2, N=8, d=128, causal=0, scale=0.1):
+    return lib.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, B, H, Hkv, N, d,
+                      causal, scale, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(o=None), dict(lse=None),
+                                dict(do=None), dict(dq=None), dict(dk=None),
+                                dict(dv=None), dict(ws=None), dict(N=0),
+                                dict(H=6, Hkv=4), dict(scale=float("nan"))])
+def test_bwd_invalid_arguments(lib, kw):
+    assert _bwd(lib, **kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_only_d128(lib):
+    assert _bwd(lib, d=64) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["q", "do", "dq", "dk", "dv", "ws"])
+def test_bwd_misaligned(lib, name):
+    assert _bwd(lib, **{name: M}) == fa.FA_ERR_MISALIGNED
