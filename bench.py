@@ -199,6 +199,26 @@ def main() -> int:
                             "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                             "frac_of_bf16_peak": round(t / BF16_PEAK_TFLOPS, 4)}
             del qq, kk, vv, oo, ll
+        # Backward of the headline workload (dQ, dK, dV from the forward's O
+        # and LSE and a seeded dO).  Throughput counts 2.5x the forward's
+        # FLOPs, the usual convention for the five products of a backward
+        # pass (the kernels recompute S and dP in both gradient kernels, so
+        # they do seven).
+        gd = torch.Generator(device=dev).manual_seed(11)
+        dout = torch.randn(q.shape, device=dev, generator=gd).to(torch.bfloat16)
+        dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
+        ws = torch.empty(2 * w.B * w.H * w.N, dtype=torch.float32, device=dev)
+        fa.forward(q, k, v, causal=w.causal, out=o, lse=lse)
+        tm_b = _time_launches(
+            lambda: fa.backward(q, k, v, o, lse, dout, causal=w.causal, dq=dq,
+                                dk=dk, dv=dv, workspace=ws), 20, 10)
+        tb = 2.5 * w.flops / (tm_b["mean"] * 1e-3) / 1e12
+        extras["bf16_n8192_backward"] = {
+            "ms": round(tm_b["mean"], 4), "ms_median": round(tm_b["median"], 4),
+            "ms_min": round(tm_b["min"], 4), "TFLOP/s": round(tb, 1),
+            "frac_of_bf16_peak": round(tb / BF16_PEAK_TFLOPS, 4),
+            "flops": "2.5 x forward (10 B H N^2 d)"}
+        del dout, dq, dk, dv, ws
         ww = workloads.WORKLOADS["fp8_n8192"]
         xq, xk, xv = (torch.from_numpy(x).to(dev)
                       for x in workloads.workload_qkv(ww))

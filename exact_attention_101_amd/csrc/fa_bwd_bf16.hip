@@ -344,8 +344,10 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
 }
 
 // ---- dK, dV: one lane per key ----
+// Two workgroups per CU (two waves per SIMD): the register budget then
+// leaves a few spills in the non-causal loop, still faster than one wave.
 template <bool CAUSAL>
-__global__ void __launch_bounds__(NTHR, 1) bwd_dkdv_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ uint4 Qr[2][ROW_ALLOC];
   __shared__ uint4 Qt[2][TR_SLOTS];
   __shared__ uint4 Or[2][ROW_ALLOC];     // dO, row layout
@@ -426,13 +428,27 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dkdv_kernel(const BwdArgs a) {
       dp = mfma(row_frag(Or[st], li, h, f), vf[f], dp);
     float p[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = 16 * (r >> 3) + 8 * h + (r & 7);   // row in the tile
-      const int q = qt0 + qi;
-      const float2 w = *reinterpret_cast<const float2*>(&Ws[st][2 * qi]);
-      const bool ok = kok && q < N && (!CAUSAL || key <= q);
-      p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -w.x)) : 0.f;
-      ds[r] = p[r] * (dp[r] - w.y);
+    for (int half = 0; half < 2; ++half) {
+      // Rows 16 half + 8 h .. + 7 of the tile: their {LSE log2 e, D} pairs
+      // are 16 consecutive floats.
+      const float4* wp =
+          reinterpret_cast<const float4*>(&Ws[st][2 * (16 * half + 8 * h)]);
+      float w[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = wp[i];
+        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z;
+        w[4 * i + 3] = x.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * half + j;
+        const int q = qt0 + 16 * half + 8 * h + j;
+        const bool ok = kok && q < N && (!CAUSAL || key <= q);
+        p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -w[2 * j])) : 0.f;
+        ds[r] = p[r] * (dp[r] - w[2 * j + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8_t pb[2], dsb[2];
     pack_b(p, pb);
