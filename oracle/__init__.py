@@ -12,6 +12,8 @@ Everything here is plain, slow and written to be read against the pages:
   pass).  This is the "classic" computation that the FlashAttention v1 post
   (DeepSchool #630), sections «Проблема базового attention» and
   «Онлайн-Softmax», says the tiled method reproduces exactly.
+  ``attention_kv`` is the same with Nq queries against Nk keys (decode,
+  bottom-right causal alignment).
 * ``attention_bwd`` -- the exact gradients dQ, dK, dV of the same
   definition for a given dO, with the softmax recomputed (the pages name
   recomputation, FlashAttention-3 summary, «Resumo do FlashAttention», and
@@ -29,7 +31,7 @@ Everything here is plain, slow and written to be read against the pages:
 Parity status of each function is stated in its module header.
 """
 
-from .attention import attention, attention_rows  # noqa: F401
+from .attention import attention, attention_kv, attention_rows  # noqa: F401
 from .attention_bwd import (  # noqa: F401
     attention_backward,
     attention_backward_sampled,

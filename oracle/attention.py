@@ -31,7 +31,10 @@ Parity status: pinned by tests/test_oracle_attention.py against a scalar
 brute-force triple loop, torch's float64 CPU attention routine, closed forms
 (zero queries, constant values, single visible key) and invariances (key
 permutation, key shift, GQA = repeated-KV MHA), and against hand-derived
-values in tests/golden/.
+values in tests/golden/.  attention_kv (Nq x Nk, bottom-right causal) is
+pinned by tests/test_oracle_decode.py: a scalar brute force, torch's
+float64 attention with an explicit mask, the square case, the last row of
+square causal attention and the merge of a key split.
 """
 
 from __future__ import annotations
@@ -46,8 +49,9 @@ def _as_f64(x) -> np.ndarray:
 
 
 def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
-          causal: bool, scale: float):
-    """One (batch, head): qh [N,d], kh/vh [N,d], rows = query indices.
+          causal: bool, scale: float, offset: int = 0):
+    """One (batch, head): qh [Nq,d], kh/vh [Nk,d], rows = query indices.
+    Causal: query i sees key j iff j <= i + offset.
     Returns O [len(rows), d] and LSE [len(rows)] in float64."""
     n_keys = kh.shape[0]
     # Scores for the selected query rows against every key: the full row of
@@ -55,7 +59,7 @@ def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
     s = scale * (qh[rows] @ kh.T)                       # [R, N]
     if causal:
         key_idx = np.arange(n_keys)[None, :]
-        s = np.where(key_idx <= rows[:, None], s, -np.inf)
+        s = np.where(key_idx <= rows[:, None] + offset, s, -np.inf)
     # Pass 1: row maximum over visible keys.
     m = s.max(axis=1)                                   # [R]
     dead = ~np.isfinite(m)                              # no visible key
@@ -66,7 +70,8 @@ def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
     with np.errstate(divide="ignore", invalid="ignore"):
         p = e / l[:, None]
     o = p @ vh                                          # [R, d]
-    lse = m_safe + np.log(l)
+    with np.errstate(divide="ignore"):                  # l = 0 where dead
+        lse = m_safe + np.log(l)
     o[dead] = 0.0
     lse[dead] = -np.inf
     return o, lse
@@ -117,3 +122,39 @@ def attention(q, k, v, *, causal: bool = False, scale=None):
     B, H, N, d = q.shape
     o, lse = attention_rows(q, k, v, np.arange(N), causal=causal, scale=scale)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def attention_kv(q, k, v, *, causal: bool = False, scale=None):
+    """Attention of Nq queries against Nk keys (decode and split-KV).
+
+    q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d].  With causal, the queries are
+    the last Nq positions of a sequence of Nk (bottom-right alignment):
+    query i sees key j iff j <= i + Nk - Nq, so a query sees no key when
+    Nq > Nk and i < Nq - Nk (O = 0, LSE = -inf there).  The pages motivate
+    this case only as long-context processing (FlashAttention-3 summary,
+    sections «Importância do Attention» and «Melhorias de desempenho do
+    FlashAttention-3»); the alignment is the plainest reading for queries
+    appended after Nk - Nq earlier positions.
+
+    Returns O [B, H, Nq, d] and LSE [B, H, Nq], float64."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch between q and k/v")
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("H must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    group = H // Hkv
+    rows = np.arange(Nq)
+    o = np.zeros((B, H, Nq, d))
+    lse = np.zeros((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            kvh = h // group
+            o[b, h], lse[b, h] = _head(q[b, h], k[b, kvh], v[b, kvh], rows,
+                                       causal, float(scale), Nk - Nq)
+    return o, lse
