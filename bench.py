@@ -219,6 +219,29 @@ def main() -> int:
             "frac_of_bf16_peak": round(tb / BF16_PEAK_TFLOPS, 4),
             "flops": "2.5 x forward (10 B H N^2 d)"}
         del dout, dq, dk, dv, ws
+        # Decode at long context through the split-KV forward: one query
+        # per head, 32 query heads on 8 KV heads, 65536 keys, B = 8.  Bound
+        # by HBM: K and V are read once (the algorithmic bytes).
+        B_, H_, Hkv_, Nk_ = 8, 32, 8, 65536
+        gk = torch.Generator(device=dev).manual_seed(13)
+        qd = torch.randn((B_, H_, 1, 128), device=dev, generator=gk).to(torch.bfloat16)
+        kd = torch.randn((B_, Hkv_, Nk_, 128), device=dev, generator=gk).to(torch.bfloat16)
+        vd = torch.randn((B_, Hkv_, Nk_, 128), device=dev, generator=gk).to(torch.bfloat16)
+        ns = fa.library().fa_splitkv_num_splits(B_, H_, Hkv_, 1, Nk_)
+        od = torch.empty_like(qd)
+        ld = torch.empty((B_, H_, 1), dtype=torch.float32, device=dev)
+        wd = torch.empty(ns * B_ * H_ * 129, dtype=torch.float32, device=dev)
+        tm_d = _time_launches(
+            lambda: fa.forward_kv(qd, kd, vd, causal=True, num_splits=ns,
+                                  out=od, lse=ld, workspace=wd), 20, 10)
+        kv_bytes = 2 * kd.numel() * 2
+        gbs = kv_bytes / (tm_d["mean"] * 1e-3) / 1e9
+        extras["decode_b8_h32_hkv8_nk65536"] = {
+            "ms": round(tm_d["mean"], 4), "ms_median": round(tm_d["median"], 4),
+            "ms_min": round(tm_d["min"], 4), "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "num_splits": ns, "bytes": "K and V once"}
+        del qd, kd, vd, od, ld, wd
         ww = workloads.WORKLOADS["fp8_n8192"]
         xq, xk, xv = (torch.from_numpy(x).to(dev)
                       for x in workloads.workload_qkv(ww))

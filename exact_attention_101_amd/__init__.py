@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "forward_kv", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -61,6 +61,11 @@ def library() -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                i32, i32, i32, i32, i32, f32, vp]
         lib.fa_bwd.restype = i32
+        lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
+                                       i32, i32, i32, i32, f32, i32, vp, vp]
+        lib.fa_fwd_splitkv.restype = i32
+        lib.fa_splitkv_num_splits.argtypes = [i32, i32, i32, i32, i32]
+        lib.fa_splitkv_num_splits.restype = i32
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i64, i32, vp, vp]
         lib.fa_fp8_quantize.restype = i32
         lib.fa_status_string.argtypes = [i32]
@@ -122,6 +127,45 @@ def forward(q, k, v, *, causal: bool = False, scale=None, out=None,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
         FA_DTYPE_BF16, _stream_handle(q.device)))
+    return out, lse
+
+
+def forward_kv(q, k, v, *, causal: bool = False, scale=None, num_splits=None,
+               out=None, lse=None, workspace=None):
+    """bf16 forward of Nq queries against Nk keys with the key range split
+    across workgroups (decode).  q: [B,H,Nq,128]; k, v: [B,Hkv,Nk,128];
+    causal uses bottom-right alignment.  Returns (o bf16 [B,H,Nq,128], lse
+    fp32 [B,H,Nq])."""
+    import torch
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or \
+                t.dtype != torch.bfloat16 or t.device != q.device:
+            raise ValueError("forward_kv expects contiguous 4-D bfloat16 "
+                             "tensors on one GPU")
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, dk = k.shape
+    if k.shape != v.shape or k.shape[0] != B or dk != d:
+        raise ValueError("k/v shape does not match q")
+    lib = library()
+    if num_splits is None:
+        num_splits = lib.fa_splitkv_num_splits(B, H, Hkv, Nq, Nk) or 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = num_splits * B * H * Nq * (d + 1)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < need or \
+            not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError(f"workspace must be a contiguous float32 tensor of "
+                         f"at least {need} elements")
+    _check(lib.fa_fwd_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+        int(num_splits), workspace.data_ptr(), _stream_handle(q.device)))
     return out, lse
 
 

@@ -13,6 +13,8 @@ namespace fa {
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
+hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
+int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
                                long long rows, uint64_t sign_lo,
                                uint64_t sign_hi, bool rotate,
@@ -142,6 +144,50 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v,
   a.c = scale * 1.4426950408889634f;
   return hip_status(
       fa::launch_bwd_bf16(a, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || H % Hkv != 0)
+    return 0;
+  return fa::splitkv_auto_splits(B, H, Hkv, Nq, Nk);
+}
+
+FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int B, int H, int Hkv,
+                             int Nq, int Nk, int d, int causal, float scale,
+                             int num_splits, float* workspace, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (H % Hkv != 0 || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (num_splits < 1 || num_splits > fa::SPLITKV_MAX_SPLITS)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(B) * H * Nq > (1LL << 40) ||
+      static_cast<long long>(B) * Hkv * Nk > (1LL << 40))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  fa::SplitArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.splits = num_splits;
+  a.c = scale * 1.4426950408889634f;
+  const long long rows = static_cast<long long>(B) * H * Nq;
+  a.ws_o = workspace;
+  a.ws_lse = workspace + rows * num_splits * 128;
+  return hip_status(fa::launch_splitkv_bf16(a, causal != 0,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,

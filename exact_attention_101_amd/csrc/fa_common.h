@@ -53,6 +53,28 @@ struct BwdArgs {
   int xcd_chunk;          // as in FwdArgs, for the dQ kernel's grid
 };
 
+// Arguments of one split-KV forward (bf16, d = 128, Nq queries against Nk
+// keys).  The workspace holds each split's normalised partial output
+// (fp32, ws_o[s][row][d]) and its log2-unit LSE (ws_lse[s][row]), rows
+// ordered (b, h, query).
+constexpr int SPLITKV_MAX_SPLITS = 256;
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int B, H, Hkv, Nq, Nk;
+  int group;              // H / Hkv
+  int splits;
+  int nrb;                // 32-row blocks per KV head (Nq * group rows)
+  long long items;        // B * Hkv * nrb * splits waves
+  long long rows_total;   // B * H * Nq
+  float c;                // scale * log2(e), signed
+};
+
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).
 __device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {

@@ -130,6 +130,43 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float scale, void* stream);
 
 /*
+ * fa_fwd_splitkv -- bf16 forward for Nq queries against Nk keys (decode and
+ *   other short-query shapes), with the key range split across workgroups
+ *   and the partial results merged by their log-sum-exp:
+ *       LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+ *   The pages motivate it as long-context processing (FlashAttention-3
+ *   summary, GeekNews, sections «Importância do Attention» and «Melhorias de
+ *   desempenho do FlashAttention-3»).
+ *   q         device, bfloat16 [B][H][Nq][d] (read only).
+ *   k, v      device, bfloat16 [B][Hkv][Nk][d] (read only).
+ *   o         device, bfloat16 [B][H][Nq][d] (written).
+ *   lse       device, float [B][H][Nq] (written, natural log; -inf for a
+ *             query that sees no key, whose o row is 0).
+ *   causal    non-zero: bottom-right alignment, query i sees key j iff
+ *             j <= i + Nk - Nq.
+ *   num_splits  1 .. 256; fa_splitkv_num_splits() gives a good value.
+ *   workspace device, float, num_splits * B * H * Nq * (d + 1) elements,
+ *             caller-owned scratch (written): the splits' partial outputs
+ *             and LSEs.  Not an output.
+ *   d         must be 128.  Other arguments as for fa_fwd.
+ *   Errors as for fa_fwd; num_splits out of range or a null workspace is
+ *   FA_ERR_INVALID_ARGUMENT, a misaligned workspace FA_ERR_MISALIGNED.
+ *   Two kernels are enqueued on `stream`.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int num_splits, float* workspace,
+                   void* stream);
+
+/*
+ * fa_splitkv_num_splits -- the split count fa_fwd_splitkv is tuned for on
+ *   this GPU for the given sizes (about 2048 waves of work, at least 4
+ *   32-key tiles per split, at most 256).  Returns 0 for invalid sizes.
+ *   Host-only; enqueues nothing.
+ */
+int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk);
+
+/*
  * fa_fp8_quantize -- optional random-sign Hadamard rotation of each row, then
  * per-tensor OCP e4m3 quantisation ("incoherent processing" of the
  * FlashAttention-3 summary, section «Baixa precisão: redução do erro de

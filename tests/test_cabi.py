@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fp8_quantize",
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv",
+              "fa_splitkv_num_splits", "fa_fp8_quantize",
               "fa_status_string",
               "fa_last_hip_error", "fa_version"):
         assert n in names
@@ -131,3 +132,32 @@ def test_bwd_only_d128(lib):
 @pytest.mark.parametrize("name", ["q", "do", "dq", "dk", "dv", "ws"])
 def test_bwd_misaligned(lib, name):
     assert _bwd(lib, **{name: M}) == fa.FA_ERR_MISALIGNED
+
+
+def _skv(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=4, Hkv=2, Nq=1, Nk=100,
+         d=128, causal=0, scale=0.1, splits=4, ws=A):
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal,
+                              scale, splits, ws, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(lse=None), dict(ws=None),
+                                dict(Nq=0), dict(Nk=0), dict(H=6, Hkv=4),
+                                dict(splits=0), dict(splits=257),
+                                dict(scale=float("inf"))])
+def test_splitkv_invalid_arguments(lib, kw):
+    assert _skv(lib, **kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_splitkv_only_d128_and_alignment(lib):
+    assert _skv(lib, d=64) == fa.FA_ERR_UNSUPPORTED
+    assert _skv(lib, ws=M) == fa.FA_ERR_MISALIGNED
+    assert _skv(lib, k=M) == fa.FA_ERR_MISALIGNED
+
+
+def test_splitkv_num_splits(lib):
+    assert lib.fa_splitkv_num_splits(0, 4, 2, 1, 100) == 0
+    for args in ((1, 32, 8, 1, 32768), (8, 32, 8, 4, 4096), (1, 4, 4, 1, 1),
+                 (64, 64, 64, 16, 1 << 20)):
+        s = lib.fa_splitkv_num_splits(*args)
+        assert 1 <= s <= 256
+        assert s <= max(1, -(-args[4] // 32) // 4)
