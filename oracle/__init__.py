@@ -13,7 +13,8 @@ Everything here is plain, slow and written to be read against the pages:
   (DeepSchool #630), sections «Проблема базового attention» and
   «Онлайн-Softmax», says the tiled method reproduces exactly.
   ``attention_kv`` is the same with Nq queries against Nk keys (decode,
-  bottom-right causal alignment).
+  bottom-right causal alignment); ``attention_varlen`` runs it per sequence
+  of a variable-length batch, with an optional sliding window.
 * ``attention_bwd`` -- the exact gradients dQ, dK, dV of the same
   definition for a given dO, with the softmax recomputed (the pages name
   recomputation, FlashAttention-3 summary, «Resumo do FlashAttention», and
@@ -31,7 +32,12 @@ Everything here is plain, slow and written to be read against the pages:
 Parity status of each function is stated in its module header.
 """
 
-from .attention import attention, attention_kv, attention_rows  # noqa: F401
+from .attention import (  # noqa: F401
+    attention,
+    attention_kv,
+    attention_rows,
+    attention_varlen,
+)
 from .attention_bwd import (  # noqa: F401
     attention_backward,
     attention_backward_sampled,

@@ -34,7 +34,11 @@ permutation, key shift, GQA = repeated-KV MHA), and against hand-derived
 values in tests/golden/.  attention_kv (Nq x Nk, bottom-right causal) is
 pinned by tests/test_oracle_decode.py: a scalar brute force, torch's
 float64 attention with an explicit mask, the square case, the last row of
-square causal attention and the merge of a key split.
+square causal attention and the merge of a key split.  attention_varlen
+(sequences of different lengths, sliding window) is pinned by
+tests/test_oracle_varlen.py: a scalar brute force, torch's float64
+attention with an explicit mask, the unwindowed case and closed forms of
+the narrowest windows.
 """
 
 from __future__ import annotations
@@ -49,17 +53,25 @@ def _as_f64(x) -> np.ndarray:
 
 
 def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
-          causal: bool, scale: float, offset: int = 0):
+          causal: bool, scale: float, offset: int = 0, left: int = -1,
+          right: int = -1):
     """One (batch, head): qh [Nq,d], kh/vh [Nk,d], rows = query indices.
-    Causal: query i sees key j iff j <= i + offset.
+    Causal: query i sees key j iff j <= i + offset.  A window (left, right
+    >= 0; -1 = unbounded) further requires i + offset - left <= j <=
+    i + offset + right.
     Returns O [len(rows), d] and LSE [len(rows)] in float64."""
     n_keys = kh.shape[0]
     # Scores for the selected query rows against every key: the full row of
     # the n x n matrix Q K^T, times the scale.
     s = scale * (qh[rows] @ kh.T)                       # [R, N]
+    key_idx = np.arange(n_keys)[None, :]
+    diag = rows[:, None] + offset
     if causal:
-        key_idx = np.arange(n_keys)[None, :]
-        s = np.where(key_idx <= rows[:, None] + offset, s, -np.inf)
+        s = np.where(key_idx <= diag, s, -np.inf)
+    if left >= 0:
+        s = np.where(key_idx >= diag - left, s, -np.inf)
+    if right >= 0:
+        s = np.where(key_idx <= diag + right, s, -np.inf)
     # Pass 1: row maximum over visible keys.
     m = s.max(axis=1)                                   # [R]
     dead = ~np.isfinite(m)                              # no visible key
@@ -158,3 +170,39 @@ def attention_kv(q, k, v, *, causal: bool = False, scale=None):
             o[b, h], lse[b, h] = _head(q[b, h], k[b, kvh], v[b, kvh], rows,
                                        causal, float(scale), Nk - Nq)
     return o, lse
+
+
+def attention_varlen(qs, ks, vs, *, causal: bool = False, window_left=-1,
+                     window_right=-1, scale=None):
+    """Attention over a batch of sequences of different lengths, each with
+    an optional sliding window.
+
+    qs: list of [H, Nq_b, d]; ks, vs: lists of [Hkv, Nk_b, d] (one entry per
+    sequence).  Sequences never see each other.  Within sequence b, with
+    off = Nk_b - Nq_b (bottom-right alignment), query i sees key j iff
+    (not causal or j <= i + off) and (window_left < 0 or j >= i + off -
+    window_left) and (window_right < 0 or j <= i + off + window_right).  A
+    query that sees no key gets O = 0, LSE = -inf.  The pages raise variable
+    masking (slow in FlashAttention, the FlashAttention-3 summary, section
+    «Comentários no Hacker News») and sliding-window attention (same
+    section) only as questions; this is the plainest reading of both.
+
+    Returns lists of O [H, Nq_b, d] and LSE [H, Nq_b], float64."""
+    outs, lses = [], []
+    for q, k, v in zip(qs, ks, vs):
+        q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+        H, Nq, d = q.shape
+        Hkv, Nk, _ = k.shape
+        if H % Hkv != 0 or k.shape != v.shape or k.shape[2] != d:
+            raise ValueError("shape mismatch")
+        sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        group = H // Hkv
+        o = np.zeros((H, Nq, d))
+        lse = np.zeros((H, Nq))
+        for h in range(H):
+            o[h], lse[h] = _head(q[h], k[h // group], v[h // group],
+                                 np.arange(Nq), causal, sc, Nk - Nq,
+                                 int(window_left), int(window_right))
+        outs.append(o)
+        lses.append(lse)
+    return outs, lses
