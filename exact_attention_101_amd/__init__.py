@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_kv", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "forward_kv", "forward_varlen", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -66,6 +66,10 @@ def library() -> ctypes.CDLL:
         lib.fa_fwd_splitkv.restype = i32
         lib.fa_splitkv_num_splits.argtypes = [i32, i32, i32, i32, i32]
         lib.fa_splitkv_num_splits.restype = i32
+        lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                      i32, i32, i32, i32, i32, i32, i32, i32,
+                                      f32, vp]
+        lib.fa_fwd_varlen.restype = i32
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i64, i32, vp, vp]
         lib.fa_fp8_quantize.restype = i32
         lib.fa_status_string.argtypes = [i32]
@@ -166,6 +170,48 @@ def forward_kv(q, k, v, *, causal: bool = False, scale=None, num_splits=None,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
         int(num_splits), workspace.data_ptr(), _stream_handle(q.device)))
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *,
+                   causal: bool = False, window=(-1, -1), scale=None, out=None,
+                   lse=None):
+    """bf16 forward over a packed batch of sequences of different lengths,
+    with an optional sliding window (left, right; -1 = unbounded).
+    q: [H, total_q, 128]; k, v: [Hkv, total_k, 128]; cu_seqlens_q/k: int32
+    CUDA tensors of B + 1 row offsets.  Returns (o bf16 [H, total_q, 128],
+    lse fp32 [H, total_q])."""
+    import torch
+    for t in (q, k, v):
+        if t.dim() != 3 or not t.is_contiguous() or not t.is_cuda or \
+                t.dtype != torch.bfloat16 or t.device != q.device:
+            raise ValueError("forward_varlen expects contiguous 3-D bfloat16 "
+                             "tensors on one GPU")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_cuda or \
+                not t.is_contiguous() or t.device != q.device:
+            raise ValueError("cu_seqlens must be contiguous int32 CUDA "
+                             "tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or \
+            cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need B + 1 entries")
+    H, total_q, d = q.shape
+    Hkv, total_k, dk = k.shape
+    if k.shape != v.shape or dk != d:
+        raise ValueError("k/v shape does not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    wl, wr = window
+    _check(library().fa_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+        cu_seqlens_q.numel() - 1, H, Hkv, total_q, total_k, int(max_seqlen_q),
+        d, int(bool(causal)), int(wl), int(wr), float(scale),
+        _stream_handle(q.device)))
     return out, lse
 
 

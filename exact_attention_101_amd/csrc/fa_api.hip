@@ -15,6 +15,7 @@ hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
+hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
                                long long rows, uint64_t sign_lo,
                                uint64_t sign_hi, bool rotate,
@@ -188,6 +189,49 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
   a.ws_lse = workspace + rows * num_splits * 128;
   return hip_status(fa::launch_splitkv_bf16(a, causal != 0,
                                             static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const int* cu_seqlens_q,
+                            const int* cu_seqlens_k, int B, int H, int Hkv,
+                            int total_q, int total_k, int max_seqlen_q, int d,
+                            int causal, int window_left, int window_right,
+                            float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || total_q <= 0 || total_k <= 0 ||
+      max_seqlen_q <= 0 || d <= 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (H % Hkv != 0 || !isfinite(scale) || window_left < -1 ||
+      window_right < -1)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(H) * total_q > (1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_MISALIGNED;
+  fa::VarlenArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.group = H / Hkv;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.max_q = max_seqlen_q;
+  a.left = window_left;
+  a.right = causal ? 0 : window_right;
+  a.c = scale * 1.4426950408889634f;
+  return hip_status(
+      fa::launch_varlen_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,

@@ -75,6 +75,27 @@ struct SplitArgs {
   float c;                // scale * log2(e), signed
 };
 
+// Arguments of one variable-length / sliding-window forward (bf16, d =
+// 128).  Rows of all sequences are packed per head: q, o [H][total_q][d],
+// k, v [Hkv][total_k][d], lse [H][total_q]; cu_q / cu_k hold B + 1 row
+// offsets (device memory).
+struct VarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* cu_q;
+  const int* cu_k;
+  int B, H, Hkv;
+  int group;              // H / Hkv
+  int total_q, total_k;
+  int max_q;              // longest query sequence (grid size)
+  int nqb;                // 128-row query blocks of the longest sequence
+  int left, right;        // window widths, -1 = unbounded (causal: right 0)
+  float c;                // scale * log2(e), signed
+};
+
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).
 __device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {

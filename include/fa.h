@@ -167,6 +167,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
 int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk);
 
 /*
+ * fa_fwd_varlen -- bf16 forward over a packed batch of sequences of
+ *   different lengths, with an optional sliding window (variable masking).
+ *   The FlashAttention-3 summary (GeekNews), section «Comentários no Hacker
+ *   News», asks about both (variable masking being slow, and sliding-window
+ *   attention).  Sequences never see each other; within sequence b, with
+ *   Nq_b, Nk_b its lengths and off = Nk_b - Nq_b (bottom-right alignment),
+ *   query i sees key j iff (window_left < 0 or j >= i + off - window_left)
+ *   and (window_right < 0 or j <= i + off + window_right); causal != 0 is
+ *   window_right = 0.  Rows that see no key get o = 0 and lse = -inf.
+ *   q, o      device, bfloat16 [H][total_q][d] (rows of all sequences
+ *             packed per head; q read only, o written).
+ *   k, v      device, bfloat16 [Hkv][total_k][d] (read only).
+ *   lse       device, float [H][total_q] (written, natural log).
+ *   cu_seqlens_q, cu_seqlens_k  device, int32 [B + 1]: sequence b owns rows
+ *             [cu[b], cu[b+1]).  Read by the kernel: a sequence whose rows
+ *             fall outside [0, total) is skipped and its outputs are left
+ *             unwritten.
+ *   max_seqlen_q  at least the longest query sequence (rows beyond it are
+ *             not computed).
+ *   window_left, window_right  >= -1 (-1 = unbounded).
+ *   d must be 128; H, Hkv, scale as for fa_fwd.  Errors as for fa_fwd;
+ *   lse and the cu_seqlens arrays need 4-byte alignment.  One kernel is
+ *   enqueued on `stream`.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int total_q, int total_k,
+                  int max_seqlen_q, int d, int causal, int window_left,
+                  int window_right, float scale, void* stream);
+
+/*
  * fa_fp8_quantize -- optional random-sign Hadamard rotation of each row, then
  * per-tensor OCP e4m3 quantisation ("incoherent processing" of the
  * FlashAttention-3 summary, section «Baixa precisão: redução do erro de

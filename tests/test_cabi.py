@@ -30,6 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv",
+              "fa_fwd_varlen",
               "fa_splitkv_num_splits", "fa_fp8_quantize",
               "fa_status_string",
               "fa_last_hip_error", "fa_version"):
@@ -161,3 +162,23 @@ def test_splitkv_num_splits(lib):
         s = lib.fa_splitkv_num_splits(*args)
         assert 1 <= s <= 256
         assert s <= max(1, -(-args[4] // 32) // 4)
+
+
+def _vl(lib, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, B=2, H=4, Hkv=2,
+        tq=100, tk=120, mq=60, d=128, causal=0, wl=-1, wr=-1, scale=0.1):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, Hkv, tq, tk, mq, d,
+                             causal, wl, wr, scale, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(cq=None), dict(ck=None),
+                                dict(B=0), dict(tq=0), dict(tk=0), dict(mq=0),
+                                dict(H=6, Hkv=4), dict(wl=-2), dict(wr=-5),
+                                dict(scale=float("nan"))])
+def test_varlen_invalid_arguments(lib, kw):
+    assert _vl(lib, **kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_only_d128_and_alignment(lib):
+    assert _vl(lib, d=64) == fa.FA_ERR_UNSUPPORTED
+    assert _vl(lib, q=M) == fa.FA_ERR_MISALIGNED
+    assert _vl(lib, cq=A + 2) == fa.FA_ERR_MISALIGNED
