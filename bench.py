@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -242,6 +243,32 @@ def main() -> int:
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "num_splits": ns, "bytes": "K and V once"}
         del qd, kd, vd, od, ld, wd
+        # Variable-length batch with a causal sliding window (4096 keys to the
+        # left): 8 sequences of 2K..16K tokens, 32 query heads on 8 KV heads.
+        # FLOPs count 4 d per visible (query, key) pair.
+        lens = [16384, 2048, 8192, 4096, 12288, 2048, 6144, 14336]
+        win = 4096
+        tot = sum(lens)
+        gv = torch.Generator(device=dev).manual_seed(17)
+        qv_ = torch.randn((32, tot, 128), device=dev, generator=gv).to(torch.bfloat16)
+        kv_ = torch.randn((8, tot, 128), device=dev, generator=gv).to(torch.bfloat16)
+        vv_ = torch.randn((8, tot, 128), device=dev, generator=gv).to(torch.bfloat16)
+        cu = torch.tensor([0] + list(itertools.accumulate(lens)),
+                          dtype=torch.int32, device=dev)
+        ov_ = torch.empty_like(qv_)
+        lv_ = torch.empty((32, tot), dtype=torch.float32, device=dev)
+        tm_v = _time_launches(
+            lambda: fa.forward_varlen(qv_, kv_, vv_, cu, cu, max(lens),
+                                      causal=True, window=(win, -1),
+                                      out=ov_, lse=lv_), 20, 10)
+        pairs = sum(sum(min(i, win) + 1 for i in range(n)) for n in lens)
+        tvl = 4 * 128 * 32 * pairs / (tm_v["mean"] * 1e-3) / 1e12
+        extras["varlen_causal_window4096"] = {
+            "ms": round(tm_v["mean"], 4), "ms_median": round(tm_v["median"], 4),
+            "ms_min": round(tm_v["min"], 4), "TFLOP/s": round(tvl, 1),
+            "frac_of_bf16_peak": round(tvl / BF16_PEAK_TFLOPS, 4),
+            "flops": "4 d per visible (query, key) pair"}
+        del qv_, kv_, vv_, ov_, lv_
         ww = workloads.WORKLOADS["fp8_n8192"]
         xq, xk, xv = (torch.from_numpy(x).to(dev)
                       for x in workloads.workload_qkv(ww))
