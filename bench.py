@@ -35,10 +35,16 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, N=8192, d=128, 1 GPU)"
 
 
+# Sources the headline kernel is built from (kernel, shared header, the
+# launching entry point): the recorded HBM counters stay valid while these
+# are unchanged.
+HEADLINE_SOURCES = ("fa_api.hip", "fa_common.h", "fa_fwd_bf16.hip")
+
+
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_101_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in HEADLINE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
