@@ -165,3 +165,35 @@ def test_outputs_only_written_in_bounds():
         torch.cuda.synchronize()
         assert torch.all(obuf[:pad] == 7.0) and torch.all(obuf[-pad:] == 7.0)
         assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[-pad:] == 7.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sampled(causal):
+    """A long sequence (N = 131072, one KV head shared by two query heads):
+    64-bit head offsets, 4096 key steps per row, sampled rows."""
+    q, k, v = workloads.qkv(1, 2, 1, 131072, 128, 81)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    o, lse = _run(*tb, causal)
+    qv, kv, vv = (workloads.bf16_values(t) for t in tb)
+    rows = sample_rows(131072, 81, n_random=6)
+    ro, rl = oracle.attention_rows(qv, kv, vv, rows, causal=causal,
+                                   heads=[(0, 0), (0, 1)])
+    _check(np.stack([o[0, h][rows] for h in (0, 1)]),
+           np.stack([lse[0, h][rows] for h in (0, 1)]), ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference(d, causal):
+    """Key norms rising 16x along the sequence with a large scale: the row
+    maximum keeps growing block after block, so the kernel's held reference
+    must move (and O, l be rescaled) many times per row."""
+    q, k, v = workloads.qkv(1, 2, 2, 1500, d, 91)
+    ramp = np.linspace(0.25, 4.0, 1500, dtype=np.float32)[None, None, :, None]
+    k = (k * ramp).astype(np.float32)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    scale = 4.0 / math.sqrt(d)
+    o, lse = _run(*tb, causal, scale=scale)
+    ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb),
+                              causal=causal, scale=scale)
+    _check(o, lse, ro, rl)
