@@ -60,9 +60,11 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdArgs a,
 // ---- dQ: one lane per query ----
 template <bool CAUSAL>
 __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
-  __shared__ uint4 Kr[2][ROW_ALLOC];
-  __shared__ uint4 Kt[2][TR_SLOTS];
-  __shared__ uint4 Vr[2][ROW_ALLOC];
+  // One array per stage and operand: every LDS read then names the array
+  // it reads, so the compiler need not wait for copies into the other stage.
+  __shared__ uint4 Kr0[ROW_ALLOC], Kr1[ROW_ALLOC];
+  __shared__ uint4 Kt0[TR_SLOTS], Kt1[TR_SLOTS];
+  __shared__ uint4 Vr0[ROW_ALLOC], Vr1[ROW_ALLOC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,40 +102,40 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
 
   const int kv_end = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (kv_end + T - 1) / T;
-  auto issue = [&](int t, int st) {
+  auto issue = [&](int t, uint4* kr, uint4* kt, uint4* vr) {
     const int r0 = t * T;
-    const auto rk = rows_rsrc(kp, r0, kv_end - r0, D * 2);
-    const auto rv = rows_rsrc(vp, r0, kv_end - r0, D * 2);
-    cp.rows(rk, Kr[st], wave);
-    cp.tr(rk, Kt[st], wave);
-    cp.rows(rv, Vr[st], wave);
+    cp.rows(kp, r0, kv_end - r0, kr, wave);
+    cp.tr(kp, r0, kv_end - r0, kt, wave);
+    cp.rows(vp, r0, kv_end - r0, vr, wave);
   };
 
   f32x16_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
 
-  issue(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
+  // Key tile t from (kr, kt, vr); tile t + 1's copies go to (nkr, nkt, nvr).
+  // Waves whose rows see none of the tile's keys still run it, fully
+  // masked (p = 0): a branch here would make the compiler wait for the
+  // copies just issued before every LDS read.
+  auto step = [&](int t, const uint4* kr, const uint4* kt, const uint4* vr,
+                  uint4* nkr, uint4* nkt, uint4* nvr) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile has landed
-    __syncthreads();                      // and every wave is done with st^1
-    if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+    __syncthreads();                      // and every wave is done with n*
+    if (t + 1 < ntiles) issue(t + 1, nkr, nkt, nvr);
     const int k0 = t * T;
-    if (CAUSAL && k0 > qw0 + T - 1) continue;   // wave's rows see no key
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-    for (int f = 0; f < 8; ++f) s = mfma(row_frag(Kr[st], li, h, f), qf[f], s);
+    for (int f = 0; f < 8; ++f) s = mfma(row_frag(kr, li, h, f), qf[f], s);
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
-      dp = mfma(row_frag(Vr[st], li, h, f), of[f], dp);
+    for (int f = 0; f < 8; ++f) dp = mfma(row_frag(vr, li, h, f), of[f], dp);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
       const bool ok = qok && key < N && (!CAUSAL || key <= qrow);
-      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -lse2))
-                         : 0.f;
+      // exp2(-inf) = 0 masks without a branch.
+      const float p = __builtin_amdgcn_exp2f(
+          ok ? fmaf(s[r], a.c, -lse2) : -__builtin_inff());
       ds[r] = p * (dp[r] - dq_row);
     }
     bf16x8_t dsb[2];
@@ -142,7 +144,13 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc[db] = mfma(tr_frag(Kt[st], trb, db, u), dsb[u], acc[db]);
+        acc[db] = mfma(tr_frag(kt, trb, db, u), dsb[u], acc[db]);
+  };
+
+  issue(0, Kr0, Kt0, Vr0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, Kr0, Kt0, Vr0, Kr1, Kt1, Vr1);
+    if (t + 1 < ntiles) step(t + 1, Kr1, Kt1, Vr1, Kr0, Kt0, Vr0);
   }
 
   if (qok) {
@@ -153,15 +161,15 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
 }
 
 // ---- dK, dV: one lane per key ----
-// Two workgroups per CU (two waves per SIMD): the register budget then
-// leaves a few spills in the non-causal loop, still faster than one wave.
+// Two workgroups per CU (two waves per SIMD), each with 256 registers.
 template <bool CAUSAL>
 __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
-  __shared__ uint4 Qr[2][ROW_ALLOC];
-  __shared__ uint4 Qt[2][TR_SLOTS];
-  __shared__ uint4 Or[2][ROW_ALLOC];     // dO, row layout
-  __shared__ uint4 Ot[2][TR_SLOTS];      // dO, transposed-read layout
-  __shared__ float Ws[2][2 * T];         // {LSE log2(e), D} of the tile rows
+  // One array per stage and operand (see the dQ kernel).
+  __shared__ uint4 Qr0[ROW_ALLOC], Qr1[ROW_ALLOC];
+  __shared__ uint4 Qt0[TR_SLOTS], Qt1[TR_SLOTS];
+  __shared__ uint4 Or0[ROW_ALLOC], Or1[ROW_ALLOC];   // dO, row layout
+  __shared__ uint4 Ot0[TR_SLOTS], Ot1[TR_SLOTS];     // dO, transposed
+  __shared__ float Ws0[2 * T], Ws1[2 * T];  // {LSE log2(e), D} of the rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,6 +196,7 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
   TileCopy cp;
   cp.init(wave, lane);
   const int trb = tr_base(lane);
+  const int rlo = row_lane(li, h);
 
   // Query tiles: every query head of the group, from the first tile that
   // holds a query >= k0 (causal) or 0.
@@ -195,22 +204,30 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
   const int ntq = (N + T - 1) / T;
   const int per_head = ntq - t0;
   const int nsteps = per_head * a.group;
-  auto issue = [&](int step, int st) {
+  struct Stage {
+    uint4* qr;
+    uint4* qt;
+    uint4* orow;
+    uint4* ot;
+    float* ws;
+  };
+  const Stage s0{Qr0, Qt0, Or0, Ot0, Ws0};
+  const Stage s1{Qr1, Qt1, Or1, Ot1, Ws1};
+
+  auto issue = [&](int step, const Stage& d) {
     const int hq = hk * a.group + step / per_head;
     const int t = t0 + step % per_head;
     const int64_t qhead = (static_cast<int64_t>(b) * a.H + hq) * N;
     const int r0 = t * T;
-    const auto rq = rows_rsrc(static_cast<const uint16_t*>(a.q) + qhead * D,
-                              r0, N - r0, D * 2);
-    const auto ro = rows_rsrc(static_cast<const uint16_t*>(a.dout) + qhead * D,
-                              r0, N - r0, D * 2);
-    cp.rows(rq, Qr[st], wave);
-    cp.tr(rq, Qt[st], wave);
-    cp.rows(ro, Or[st], wave);
-    cp.tr(ro, Ot[st], wave);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qhead * D;
+    const uint16_t* op = static_cast<const uint16_t*>(a.dout) + qhead * D;
+    cp.rows(qp, r0, N - r0, d.qr, wave);
+    cp.tr(qp, r0, N - r0, d.qt, wave);
+    cp.rows(op, r0, N - r0, d.orow, wave);
+    cp.tr(op, r0, N - r0, d.ot, wave);
     if (wave == 0) {
       const auto rw = rows_rsrc(a.ws + 2 * qhead, r0, N - r0, 8);
-      copy4(rw, Ws[st], 4u * lane);
+      copy4(rw, d.ws, 4u * lane);
     }
   };
 
@@ -221,27 +238,32 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
     dv[i] = f32x16_t{};
   }
 
-  if (nsteps > 0) issue(0, 0);
-  for (int step = 0; step < nsteps; ++step) {
-    const int st = step & 1;
+  // Query tile `step` from c; the next one's copies go to n.  Waves whose
+  // keys no query of the tile sees (causal) still run it, fully masked.
+  auto run = [&](int step, const Stage& c, const Stage& n) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (step + 1 < nsteps) issue(step + 1, st ^ 1);
+    if (step + 1 < nsteps) issue(step + 1, n);
     const int qt0 = (t0 + step % per_head) * T;
-    if (CAUSAL && qt0 + T - 1 < kw0) continue;   // no query sees these keys
+    // LDS read addresses (the four d-block variants of the transposed one,
+    // the row-layout ones of the two tiles, the {LSE, D} one) are formed
+    // here from opaque copies the compiler cannot hoist, so that they hold
+    // registers only while used: the loop needs every register it has.
+    int tb = trb, ro = rlo, wo = 16 * h;
+    asm volatile("" : "+v"(tb), "+v"(ro), "+v"(wo));
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-    for (int f = 0; f < 8; ++f) s = mfma(row_frag(Qr[st], li, h, f), kf[f], s);
+    for (int f = 0; f < 8; ++f) s = mfma(row_frag_at(c.qr, ro, f), kf[f], s);
 #pragma unroll
     for (int f = 0; f < 8; ++f)
-      dp = mfma(row_frag(Or[st], li, h, f), vf[f], dp);
-    float p[16], ds[16];
+      dp = mfma(row_frag_at(c.orow, ro, f), vf[f], dp);
+    // Rows 16 u + 8 h .. + 7 of the tile (k-step u of the dV / dK MFMAs):
+    // their {LSE log2 e, D} pairs are 16 consecutive floats.  Each half is
+    // packed and fed to the matrix core as soon as it is formed.
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // Rows 16 half + 8 h .. + 7 of the tile: their {LSE log2 e, D} pairs
-      // are 16 consecutive floats.
+    for (int u = 0; u < 2; ++u) {
       const float4* wp =
-          reinterpret_cast<const float4*>(&Ws[st][2 * (16 * half + 8 * h)]);
+          reinterpret_cast<const float4*>(&c.ws[32 * u + wo]);
       float w[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -249,26 +271,35 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
         w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z;
         w[4 * i + 3] = x.w;
       }
+      // Only the causal mask is applied.  Query rows past N arrive as
+      // zeros (Q, dO and their {LSE, D} pair), so their p = 1 meets
+      // dO = 0 and dP - D = 0 and adds nothing; keys past N are not stored.
+      float p[8], ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 8 * half + j;
-        const int q = qt0 + 16 * half + 8 * h + j;
-        const bool ok = kok && q < N && (!CAUSAL || key <= q);
-        p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -w[2 * j])) : 0.f;
-        ds[r] = p[r] * (dp[r] - w[2 * j + 1]);
+        const int r = 8 * u + j;
+        const float x = fmaf(s[r], a.c, -w[2 * j]);
+        // exp2(-inf) = 0 masks without a branch.
+        p[j] = __builtin_amdgcn_exp2f(
+            (!CAUSAL || key <= qt0 + 16 * u + 8 * h + j) ? x
+                                                         : -__builtin_inff());
+        ds[j] = p[j] * (dp[r] - w[2 * j + 1]);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t pb, dsb;
+      pack8(p, pb);
+      pack8(ds, dsb);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = mfma(tr_frag(c.ot, tb, db, u), pb, dv[db]);
+        dk[db] = mfma(tr_frag(c.qt, tb, db, u), dsb, dk[db]);
+      }
     }
-    bf16x8_t pb[2], dsb[2];
-    pack_b(p, pb);
-    pack_b(ds, dsb);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        dv[db] = mfma(tr_frag(Ot[st], trb, db, u), pb[u], dv[db]);
-        dk[db] = mfma(tr_frag(Qt[st], trb, db, u), dsb[u], dk[db]);
-      }
+  };
+
+  if (nsteps > 0) issue(0, s0);
+  for (int step = 0; step < nsteps; step += 2) {
+    run(step, s0, s1);
+    if (step + 1 < nsteps) run(step + 1, s1, s0);
   }
 
   if (kok) {

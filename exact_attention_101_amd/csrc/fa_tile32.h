@@ -4,12 +4,16 @@
 // masked / variable-length forward).  Internal header.
 //
 // LDS layouts of a 32-row tile (rows are keys or queries, 16-byte chunks):
-//   row layout: row r at chunks r * 17 .. r * 17 + 15 (one pad chunk per row)
-//     for the row fragments, read in sigma order;
+//   row layout: row r = 16 g + i, chunk c stored at chunk 256 g + 16 c + i
+//     (chunk-major within each 16-row group), so the 16 lanes that read
+//     chunk c of 16 rows for a row fragment hit 16 consecutive chunks;
 //   transposed-read layout: row r, chunk c stored at chunk
 //     r * 16 + ((c / 4) ^ (r % 4)) * 4 + c % 4, for ds_read_b64_tr_b16.
-// Tiles arrive by buffer_load_dwordx4 ... lds; rows past the descriptor's
-// end read zeros.
+// Tiles arrive by buffer_load_dwordx4 ... lds, eight 64-lane copies per
+// tile, two per wave: copy i of a wave covers rows 16 i .. 16 i + 15 and is
+// addressed through a descriptor that starts at row 16 i, so a wave needs
+// one per-lane offset per layout for all its copies.  Rows past the
+// descriptor's end read zeros.
 #pragma once
 
 #include "fa_common.h"
@@ -19,19 +23,13 @@ namespace {
 
 constexpr int D = 128;
 constexpr int NCH = D / 8;                  // 16-byte chunks per row
-constexpr int KSL = NCH + 1;                // padded row stride, chunks
 constexpr int T = 32;                       // rows per tile (one step)
 constexpr int NW = 4;                       // waves per workgroup
 constexpr int NTHR = 64 * NW;
 constexpr int BLK = T * NW;                 // rows per workgroup (128)
-constexpr int ROW_SLOTS = T * KSL;          // 544
-constexpr int ROW_COPIES = (ROW_SLOTS + 63) / 64;   // 9 (the last partly pad)
-constexpr int ROW_ALLOC = ROW_COPIES * 64;  // 576 chunks
-constexpr int TR_SLOTS = T * NCH;           // 512
-constexpr int TR_COPIES = TR_SLOTS / 64;    // 8
-constexpr int ROW_PW = (ROW_COPIES + NW - 1) / NW;  // 3 (wave 0), others 2
-constexpr int TR_PW = TR_COPIES / NW;               // 2
-constexpr uint32_t FAR = 0x80000000u;       // past any descriptor: reads 0
+constexpr int ROW_ALLOC = T * NCH;          // 512 chunks, row layout
+constexpr int TR_SLOTS = T * NCH;           // 512 chunks, transposed layout
+constexpr int HALF_ROWS = 16;               // rows per copy group
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -80,47 +78,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base,
       max(rows, 0) * row_bytes, 0x00020000);
 }
 
-// Per-lane global byte offsets of the copies one wave issues for a 32-row
-// tile of 256-byte rows: row layout (copies wave, wave + 4, wave + 8) and
-// transposed-read layout (copies wave, wave + 4).
+// Per-lane global byte offsets of the two 64-lane copies one wave issues
+// for each layout of a 32-row tile of 256-byte rows.  Copy i covers rows
+// 16 i .. 16 i + 15 and reads through a descriptor based at row 16 i, so
+// both copies share the offset:
+//   row layout, wave w: lane L reads row L % 16, chunk 4 w + L / 16, and
+//     writes LDS chunk 256 i + 64 w + L = the layout's slot for that chunk;
+//   transposed layout, wave w: lane L reads row 4 w + L / 16, chunk
+//     c(L) with c's 4-chunk group swizzled by the row (row % 4 = L / 16),
+//     and writes LDS chunk 256 i + 64 w + L.
 struct TileCopy {
-  uint32_t row_off[ROW_PW];
-  uint32_t tr_off[TR_PW];
-  int nrow;                                  // row-layout copies of this wave
+  uint32_t row_v;
+  uint32_t tr_v;
 
   __device__ void init(int wave, int lane) {
-    nrow = 0;
-#pragma unroll
-    for (int i = 0; i < ROW_PW; ++i) {
-      const int j = wave + NW * i;
-      const int slot = 64 * j + lane;
-      const int r = slot / KSL, c = slot % KSL;
-      row_off[i] = (j < ROW_COPIES && r < T && c < NCH)
-                       ? static_cast<uint32_t>(r * D * 2 + c * 16)
-                       : FAR;
-      if (j < ROW_COPIES) nrow = i + 1;
-    }
-#pragma unroll
-    for (int i = 0; i < TR_PW; ++i) {
-      const int slot = 64 * (wave + NW * i) + lane;
-      const int r = slot / NCH, p = slot % NCH;
-      const int c = (((p >> 2) ^ (r & 3)) << 2) | (p & 3);
-      tr_off[i] = static_cast<uint32_t>(r * D * 2 + c * 16);
-    }
+    const int q = lane >> 4, p = lane & 15;
+    row_v = static_cast<uint32_t>(p * D * 2 + (4 * wave + q) * 16);
+    const int c = (((p >> 2) ^ q) << 2) | (p & 3);
+    tr_v = static_cast<uint32_t>((4 * wave + q) * D * 2 + c * 16);
   }
 
-  __device__ void rows(__amdgpu_buffer_rsrc_t rs, const uint4* dst,
-                       int wave) const {
+  // Copies of rows r0 .. r0 + 31 of `base` (rows_left rows exist from r0).
+  __device__ void rows(const void* base, int r0, int rows_left,
+                       const uint4* dst, int wave) const {
 #pragma unroll
-    for (int i = 0; i < ROW_PW; ++i)
-      if (i < ROW_COPIES / NW || i < nrow)
-        copy16(rs, dst + 64 * (wave + NW * i), row_off[i]);
+    for (int i = 0; i < 2; ++i)
+      copy16(rows_rsrc(base, r0 + HALF_ROWS * i, rows_left - HALF_ROWS * i,
+                       D * 2),
+             dst + 256 * i + 64 * wave, row_v);
   }
-  __device__ void tr(__amdgpu_buffer_rsrc_t rs, const uint4* dst,
-                     int wave) const {
+  __device__ void tr(const void* base, int r0, int rows_left,
+                     const uint4* dst, int wave) const {
 #pragma unroll
-    for (int i = 0; i < TR_PW; ++i)
-      copy16(rs, dst + 64 * (wave + NW * i), tr_off[i]);
+    for (int i = 0; i < 2; ++i)
+      copy16(rows_rsrc(base, r0 + HALF_ROWS * i, rows_left - HALF_ROWS * i,
+                       D * 2),
+             dst + 256 * i + 64 * wave, tr_v);
   }
 };
 
@@ -151,9 +144,18 @@ __device__ __forceinline__ bf16x8_t tr_frag(const uint4* tile, int base,
 
 // A operand from a row-layout tile: row sigma(li) of the tile, d chunk
 // 8 h + s (k-step s covers d = 8 s .. 8 s + 7 and 64 + 8 s .. 64 + 8 s + 7).
+// sigma keeps bit 4 of li, so the row stays in li's 16-row group.
+// row_lane gives the lane's chunk offset for k-step 0; step s adds 16 s.
+__device__ __forceinline__ int row_lane(int li, int h) {
+  return 256 * (li >> 4) + 128 * h + (sigma(li) & 15);
+}
+__device__ __forceinline__ bf16x8_t row_frag_at(const uint4* tile, int lo,
+                                                int s) {
+  return as_bf16x8(tile[lo + 16 * s]);
+}
 __device__ __forceinline__ bf16x8_t row_frag(const uint4* tile, int li, int h,
                                              int s) {
-  return as_bf16x8(tile[sigma(li) * KSL + 8 * h + s]);
+  return row_frag_at(tile, row_lane(li, h), s);
 }
 
 // B-operand register fragments of one 128-wide row (query or key) for the
@@ -186,6 +188,17 @@ __device__ __forceinline__ void store_rows(uint16_t* dst,
       *reinterpret_cast<uint4*>(dst + 32 * db + 16 * u + 8 * h) = w;
     }
   }
+}
+
+// Pack 8 fp32 values (rows 16 u + 8 h .. + 7 of an S-shaped accumulator)
+// into the bf16 B operand of k-step u.
+__device__ __forceinline__ void pack8(const float (&x)[8], bf16x8_t& b) {
+  uint4 w;
+  w.x = pack_bf16x2(x[0], x[1]);
+  w.y = pack_bf16x2(x[2], x[3]);
+  w.z = pack_bf16x2(x[4], x[5]);
+  w.w = pack_bf16x2(x[6], x[7]);
+  b = as_bf16x8(w);
 }
 
 // Pack 16 fp32 values of an S-shaped accumulator (register r <-> tile row
