@@ -4,16 +4,17 @@
 // masked / variable-length forward).  Internal header.
 //
 // LDS layouts of a 32-row tile (rows are keys or queries, 16-byte chunks):
-//   row layout: row r = 16 g + i, chunk c stored at chunk 256 g + 16 c + i
-//     (chunk-major within each 16-row group), so the 16 lanes that read
-//     chunk c of 16 rows for a row fragment hit 16 consecutive chunks;
+//   row layout: row r = 8 g + i, chunk c stored at chunk 136 g + 8 c + i
+//     (chunk-major within each 8-row group, groups 136 chunks apart): the
+//     16 lanes that read chunk c of rows 0..15 (or 16..31) for a row
+//     fragment hit 16 different 16-byte bank slots, and a k-step moves the
+//     address by a constant;
 //   transposed-read layout: row r, chunk c stored at chunk
 //     r * 16 + ((c / 4) ^ (r % 4)) * 4 + c % 4, for ds_read_b64_tr_b16.
 // Tiles arrive by buffer_load_dwordx4 ... lds, eight 64-lane copies per
-// tile, two per wave: copy i of a wave covers rows 16 i .. 16 i + 15 and is
-// addressed through a descriptor that starts at row 16 i, so a wave needs
-// one per-lane offset per layout for all its copies.  Rows past the
-// descriptor's end read zeros.
+// tile, two per wave, each reading whole 128-byte lines.  A wave's copies
+// share one per-lane offset per layout; what differs between them goes into
+// the buffer descriptor's base.  Rows past the descriptor's end read zeros.
 #pragma once
 
 #include "fa_common.h"
@@ -27,9 +28,10 @@ constexpr int T = 32;                       // rows per tile (one step)
 constexpr int NW = 4;                       // waves per workgroup
 constexpr int NTHR = 64 * NW;
 constexpr int BLK = T * NW;                 // rows per workgroup (128)
-constexpr int ROW_ALLOC = T * NCH;          // 512 chunks, row layout
+constexpr int RG = 136;                     // row layout: group stride
+constexpr int ROW_ALLOC = 3 * RG + 8 * NCH; // 536 chunks, row layout
 constexpr int TR_SLOTS = T * NCH;           // 512 chunks, transposed layout
-constexpr int HALF_ROWS = 16;               // rows per copy group
+constexpr int HALF_ROWS = 16;               // rows per descriptor
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -79,21 +81,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base,
 }
 
 // Per-lane global byte offsets of the two 64-lane copies one wave issues
-// for each layout of a 32-row tile of 256-byte rows.  Copy i covers rows
-// 16 i .. 16 i + 15 and reads through a descriptor based at row 16 i, so
-// both copies share the offset:
-//   row layout, wave w: lane L reads row L % 16, chunk 4 w + L / 16, and
-//     writes LDS chunk 256 i + 64 w + L = the layout's slot for that chunk;
-//   transposed layout, wave w: lane L reads row 4 w + L / 16, chunk
-//     c(L) with c's 4-chunk group swizzled by the row (row % 4 = L / 16),
-//     and writes LDS chunk 256 i + 64 w + L.
+// for each layout of a 32-row tile of 256-byte rows:
+//   row layout, wave w, copy k: 8-row group w, chunks 8 k .. 8 k + 7; lane
+//     L reads row 8 w + L % 8, chunk 8 k + L / 8 and writes LDS chunk
+//     136 w + 64 k + L.  The descriptor starts at row 16 (w / 2) and, for
+//     k = 1, 128 bytes further;
+//   transposed layout, wave w, copy i: lane L reads row 4 w + 16 i + L / 16,
+//     chunk c(L) with c's 4-chunk group swizzled by the row (row % 4 =
+//     L / 16), and writes LDS chunk 256 i + 64 w + L.  The descriptor starts
+//     at row 16 i.
 struct TileCopy {
   uint32_t row_v;
   uint32_t tr_v;
 
   __device__ void init(int wave, int lane) {
+    row_v = static_cast<uint32_t>((8 * (wave & 1) + (lane & 7)) * D * 2 +
+                                  (lane >> 3) * 16);
     const int q = lane >> 4, p = lane & 15;
-    row_v = static_cast<uint32_t>(p * D * 2 + (4 * wave + q) * 16);
     const int c = (((p >> 2) ^ q) << 2) | (p & 3);
     tr_v = static_cast<uint32_t>((4 * wave + q) * D * 2 + c * 16);
   }
@@ -101,11 +105,21 @@ struct TileCopy {
   // Copies of rows r0 .. r0 + 31 of `base` (rows_left rows exist from r0).
   __device__ void rows(const void* base, int r0, int rows_left,
                        const uint4* dst, int wave) const {
+    const int h16 = HALF_ROWS * (wave >> 1);
+    const int bytes = max(rows_left - h16, 0) * D * 2;
+    const char* b = static_cast<const char*>(base) +
+                    static_cast<int64_t>(r0 + h16) * D * 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      copy16(rows_rsrc(base, r0 + HALF_ROWS * i, rows_left - HALF_ROWS * i,
-                       D * 2),
-             dst + 256 * i + 64 * wave, row_v);
+    for (int k = 0; k < 2; ++k) {
+      // readfirstlane keeps the (uniform) size scalar: a saturating
+      // subtract would otherwise go to a vector register and force a
+      // per-lane loop around the copy.
+      const int rec = __builtin_amdgcn_readfirstlane(
+          bytes > 128 * k ? bytes - 128 * k : 0);
+      copy16(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b + 128 * k),
+                                               0, rec, 0x00020000),
+             dst + RG * wave + 64 * k, row_v);
+    }
   }
   __device__ void tr(const void* base, int r0, int rows_left,
                      const uint4* dst, int wave) const {
@@ -144,14 +158,14 @@ __device__ __forceinline__ bf16x8_t tr_frag(const uint4* tile, int base,
 
 // A operand from a row-layout tile: row sigma(li) of the tile, d chunk
 // 8 h + s (k-step s covers d = 8 s .. 8 s + 7 and 64 + 8 s .. 64 + 8 s + 7).
-// sigma keeps bit 4 of li, so the row stays in li's 16-row group.
-// row_lane gives the lane's chunk offset for k-step 0; step s adds 16 s.
+// row_lane gives the lane's chunk offset for k-step 0; step s adds 8 s.
 __device__ __forceinline__ int row_lane(int li, int h) {
-  return 256 * (li >> 4) + 128 * h + (sigma(li) & 15);
+  const int r = sigma(li);
+  return RG * (r >> 3) + 64 * h + (r & 7);
 }
 __device__ __forceinline__ bf16x8_t row_frag_at(const uint4* tile, int lo,
                                                 int s) {
-  return as_bf16x8(tile[lo + 16 * s]);
+  return as_bf16x8(tile[lo + 8 * s]);
 }
 __device__ __forceinline__ bf16x8_t row_frag(const uint4* tile, int li, int h,
                                              int s) {

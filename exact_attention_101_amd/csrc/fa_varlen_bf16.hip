@@ -18,8 +18,8 @@
 // 32 rows (one lane per row), 32-key tiles of K (row layout) and V
 // (transposed-read layout) streamed through LDS by DMA, double-buffered, as
 // in the backward's dQ kernel.  Only the tiles the workgroup's rows can see
-// are loaded and computed, so the cost follows the window, not the sequence
-// length.  Per tile:
+// are loaded, and a wave skips the arithmetic of tiles its own rows cannot
+// see, so the cost follows the window, not the sequence length.  Per tile:
 // S^T = K Q^T and O^T += V^T P^T on MFMA in the forward kernel's layouts,
 // with an exact online softmax (running maximum and sum over both lane
 // halves, rescale of O).  The grid covers the longest sequence; workgroups
@@ -86,6 +86,11 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
   const int t0 = lo / T;
   const int t1 = hi < lo ? t0 : hi / T + 1;  // tiles [t0, t1)
   const int iw0 = i0 + T * wave;
+  const int iw1 = min(i1, iw0 + T - 1);
+  const bool wave_rows = iw0 <= i1;
+  const int wlo = wave_rows ? key_lo(iw0) : 0;
+  const int whi = wave_rows ? key_hi(iw1) : -1;
+
   const int qi = iw0 + li;                   // this lane's query row
   const bool qok = qi < Nq;
   const int64_t qrow = static_cast<int64_t>(hq) * a.total_q + q_beg + qi;
@@ -113,15 +118,17 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
   float m = -__builtin_inff();
   float l = 0.f;
 
-  // A wave none of whose rows sees the tile still runs it, fully masked:
-  // a branch between the copies of tile t + 1 and the reads of tile t
-  // would make the compiler wait for those copies before every read.
+  // The skip below makes the compiler wait for tile t + 1's copies before
+  // the reads of tile t (it cannot tell the stages apart after the branch);
+  // with three workgroups per CU that wait costs less than computing
+  // masked tiles would.
   auto tile = [&](int t, const uint4* kt, const uint4* vt, uint4* kn,
                   uint4* vn) {
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): tile t landed
     __syncthreads();                         // every wave is done with kn/vn
     if (t + 1 < t1) issue(t + 1, kn, vn);
     const int k0 = t * T;
+    if (k0 > whi || k0 + T - 1 < wlo) return;   // no row of this wave sees it
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
