@@ -14,7 +14,8 @@ Everything here is plain, slow and written to be read against the pages:
   «Онлайн-Softmax», says the tiled method reproduces exactly.
   ``attention_kv`` is the same with Nq queries against Nk keys (decode,
   bottom-right causal alignment); ``attention_varlen`` runs it per sequence
-  of a variable-length batch, with an optional sliding window.
+  of a variable-length batch, with an optional sliding window;
+  ``attention_masked`` takes an arbitrary boolean visibility mask.
 * ``attention_bwd`` -- the exact gradients dQ, dK, dV of the same
   definition for a given dO, with the softmax recomputed (the pages name
   recomputation, FlashAttention-3 summary, «Resumo do FlashAttention», and
@@ -35,6 +36,7 @@ Parity status of each function is stated in its module header.
 from .attention import (  # noqa: F401
     attention,
     attention_kv,
+    attention_masked,
     attention_rows,
     attention_varlen,
 )

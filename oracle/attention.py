@@ -38,7 +38,10 @@ square causal attention and the merge of a key split.  attention_varlen
 (sequences of different lengths, sliding window) is pinned by
 tests/test_oracle_varlen.py: a scalar brute force, torch's float64
 attention with an explicit mask, the unwindowed case and closed forms of
-the narrowest windows.
+the narrowest windows.  attention_masked (an arbitrary boolean mask) is
+pinned by tests/test_oracle_masked.py: a scalar brute force, torch's
+float64 attention with the same mask, and the causal, windowed and
+all-visible masks against the oracle's own closed-form paths.
 """
 
 from __future__ import annotations
@@ -54,11 +57,12 @@ def _as_f64(x) -> np.ndarray:
 
 def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
           causal: bool, scale: float, offset: int = 0, left: int = -1,
-          right: int = -1):
+          right: int = -1, allow=None):
     """One (batch, head): qh [Nq,d], kh/vh [Nk,d], rows = query indices.
     Causal: query i sees key j iff j <= i + offset.  A window (left, right
     >= 0; -1 = unbounded) further requires i + offset - left <= j <=
-    i + offset + right.
+    i + offset + right.  allow, if given, is a boolean [len(rows), Nk]
+    array: key j is visible to row r only where allow[r, j] is true.
     Returns O [len(rows), d] and LSE [len(rows)] in float64."""
     n_keys = kh.shape[0]
     # Scores for the selected query rows against every key: the full row of
@@ -72,6 +76,8 @@ def _head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: np.ndarray,
         s = np.where(key_idx >= diag - left, s, -np.inf)
     if right >= 0:
         s = np.where(key_idx <= diag + right, s, -np.inf)
+    if allow is not None:
+        s = np.where(allow, s, -np.inf)
     # Pass 1: row maximum over visible keys.
     m = s.max(axis=1)                                   # [R]
     dead = ~np.isfinite(m)                              # no visible key
@@ -206,3 +212,44 @@ def attention_varlen(qs, ks, vs, *, causal: bool = False, window_left=-1,
         outs.append(o)
         lses.append(lse)
     return outs, lses
+
+
+def attention_masked(q, k, v, mask, *, scale=None, rows=None):
+    """Attention under an arbitrary visibility mask.
+
+    q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d]; mask: boolean array that
+    broadcasts to [B, H, Nq, Nk] (size-1 batch or head axes are shared):
+    query i of (b, h) sees key j iff mask[b, h, i, j].  A query that sees no
+    key gets O = 0, LSE = -inf.  The pages raise arbitrary and variable
+    masks only as a question (FlashAttention-3 summary, section
+    «Comentários no Hacker News»: FlashAttention is said to be much slower
+    with them); the plainest reading is the softmax over the visible keys
+    only, which is what masking scores to -inf gives.  rows (optional) picks
+    the query rows to evaluate, for every (b, h).
+
+    Returns O [B, H, R, d] and LSE [B, H, R] (R = Nq or len(rows)), float64.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch between q and k/v")
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError("H must be a multiple of Hkv")
+    mask = np.asarray(mask, dtype=bool)
+    if mask.ndim != 4:
+        raise ValueError("mask must have 4 axes [B|1, H|1, Nq, Nk]")
+    mask = np.broadcast_to(mask, (B, H, Nq, Nk))
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, np.int64)
+    group = H // Hkv
+    o = np.zeros((B, H, len(rows), d))
+    lse = np.zeros((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            kvh = h // group
+            o[b, h], lse[b, h] = _head(q[b, h], k[b, kvh], v[b, kvh], rows,
+                                       False, sc, allow=mask[b, h][rows])
+    return o, lse

@@ -117,3 +117,44 @@ def bf16_values(t) -> np.ndarray:
     values (widening is exact)."""
     import torch
     return t.detach().to("cpu").to(torch.float32).numpy()
+
+
+def pack_mask(mask) -> np.ndarray:
+    """Boolean visibility mask [..., Nq, Nk] -> uint32 [..., Nq, ceil(Nk/32)]
+    words: bit j % 32 of word j // 32 is set iff key j is visible.  A data
+    format conversion only (the HIP path reads masks in this form)."""
+    m = np.asarray(mask, dtype=bool)
+    nk = m.shape[-1]
+    nw = (nk + 31) // 32
+    pad = np.zeros(m.shape[:-1] + (nw * 32,), dtype=bool)
+    pad[..., :nk] = m
+    bits = pad.reshape(m.shape[:-1] + (nw, 32)).astype(np.uint64)
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (bits * weights).sum(axis=-1).astype(np.uint32)
+
+
+def random_mask(shape, p_visible: float, seed: int) -> np.ndarray:
+    """Independent Bernoulli(p_visible) visibility per (query, key)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.random(shape) < p_visible
+
+
+def block_sparse_mask(Nq: int, Nk: int, block: int, n_random: int,
+                      seed: int) -> np.ndarray:
+    """Boolean [Nq, Nk] mask made of block x block squares: query block i
+    sees key block 0 (global), key blocks i - 1, i, i + 1 (local band) and
+    n_random further key blocks drawn without replacement (seeded)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nqb = (Nq + block - 1) // block
+    nkb = (Nk + block - 1) // block
+    m = np.zeros((Nq, Nk), dtype=bool)
+    for i in range(nqb):
+        keep = {0, i - 1, i, i + 1}
+        rest = [j for j in range(nkb) if j not in keep]
+        pick = rng.choice(len(rest), size=min(n_random, len(rest)),
+                          replace=False)
+        keep |= {rest[t] for t in pick}
+        for j in keep:
+            if 0 <= j < nkb:
+                m[i * block:(i + 1) * block, j * block:(j + 1) * block] = True
+    return m
