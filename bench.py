@@ -164,6 +164,7 @@ def main() -> int:
         return 2
     rank = int(os.environ.get("RANK", "0"))
 
+    import numpy as np
     import torch
     import exact_attention_101_amd as fa
     import workloads
@@ -275,6 +276,32 @@ def main() -> int:
             "frac_of_bf16_peak": round(tvl / BF16_PEAK_TFLOPS, 4),
             "flops": "4 d per visible (query, key) pair"}
         del qv_, kv_, vv_, ov_, lv_
+        # Arbitrary masks on the headline shape (B4 H16 N8192 d128), one
+        # mask shared by every (batch, head): a block-sparse pattern of
+        # 128 x 128 squares (key block 0, the local band of three blocks and
+        # 8 random blocks per query block), and the all-visible mask, whose
+        # time against the unmasked kernel is the cost of masking itself.
+        # FLOPs count 4 d per visible (query, key) pair.
+        for mname, mbool in (
+                ("masked_block_sparse_n8192",
+                 workloads.block_sparse_mask(w.N, w.N, 128, 8, 23)),
+                ("masked_all_visible_n8192",
+                 np.ones((w.N, w.N), dtype=bool))):
+            mw_ = torch.from_numpy(workloads.pack_mask(mbool)[None, None]
+                                   .view(np.int32)).to(dev)
+            tm_m = _time_launches(
+                lambda: fa.forward_masked(q, k, v, mw_, out=o, lse=lse),
+                20, 10)
+            vis = float(mbool.sum())
+            tmk = 4 * w.d * w.B * w.H * vis / (tm_m["mean"] * 1e-3) / 1e12
+            extras[mname] = {
+                "ms": round(tm_m["mean"], 4),
+                "ms_median": round(tm_m["median"], 4),
+                "ms_min": round(tm_m["min"], 4), "TFLOP/s": round(tmk, 1),
+                "frac_of_bf16_peak": round(tmk / BF16_PEAK_TFLOPS, 4),
+                "visible_fraction": round(vis / float(w.N) ** 2, 4),
+                "flops": "4 d per visible (query, key) pair"}
+            del mw_
         ww = workloads.WORKLOADS["fp8_n8192"]
         xq, xk, xv = (torch.from_numpy(x).to(dev)
                       for x in workloads.workload_qkv(ww))

@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_kv", "forward_varlen", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "forward_kv", "forward_varlen", "forward_masked", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -70,6 +70,9 @@ def library() -> ctypes.CDLL:
                                       i32, i32, i32, i32, i32, i32, i32, i32,
                                       f32, vp]
         lib.fa_fwd_varlen.restype = i32
+        lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32,
+                                      i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_fwd_masked.restype = i32
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i64, i32, vp, vp]
         lib.fa_fp8_quantize.restype = i32
         lib.fa_status_string.argtypes = [i32]
@@ -212,6 +215,46 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *,
         cu_seqlens_q.numel() - 1, H, Hkv, total_q, total_k, int(max_seqlen_q),
         d, int(bool(causal)), int(wl), int(wr), float(scale),
         _stream_handle(q.device)))
+    return out, lse
+
+
+def forward_masked(q, k, v, mask, *, scale=None, out=None, lse=None):
+    """bf16 forward under an arbitrary visibility mask.  q: [B, H, Nq, 128];
+    k, v: [B, Hkv, Nk, 128]; mask: int32 (or uint32) CUDA tensor of packed
+    bits [Bm, Hm, Nq, ceil(Nk / 32)] with Bm in (1, B) and Hm in (1, H) (a
+    size-1 axis is shared): bit j % 32 of word j // 32 of row i set means
+    query i sees key j.  Returns (o bf16 [B, H, Nq, 128], lse fp32
+    [B, H, Nq]); rows that see no key get o = 0, lse = -inf."""
+    import torch
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or \
+                t.dtype != torch.bfloat16 or t.device != q.device:
+            raise ValueError("forward_masked expects contiguous 4-D bfloat16 "
+                             "tensors on one GPU")
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if k.shape != v.shape or Bk != B or dk != d:
+        raise ValueError("k/v shape does not match q")
+    W = (Nk + 31) // 32
+    if mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)) \
+            or mask.dim() != 4 or not mask.is_contiguous() or \
+            not mask.is_cuda or mask.device != q.device:
+        raise ValueError("mask must be a contiguous 4-D int32 CUDA tensor")
+    Bm, Hm, Nqm, Wm = mask.shape
+    if Bm not in (1, B) or Hm not in (1, H) or Nqm != Nq or Wm != W:
+        raise ValueError(f"mask must be [1|{B}, 1|{H}, {Nq}, {W}]")
+    bstride = Hm * Nq * W if (Bm == B and B > 1) else 0
+    hstride = Nq * W if (Hm == H and H > 1) else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(library().fa_fwd_masked(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), mask.data_ptr(), bstride, hstride, B, H, Hkv, Nq, Nk,
+        d, float(scale), _stream_handle(q.device)))
     return out, lse
 
 

@@ -16,6 +16,7 @@ hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
 hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream);
+hipError_t launch_masked_bf16(MaskArgs a, hipStream_t stream);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
                                long long rows, uint64_t sign_lo,
                                uint64_t sign_hi, bool rotate,
@@ -232,6 +233,42 @@ FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v,
   a.c = scale * 1.4426950408889634f;
   return hip_status(
       fa::launch_varlen_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_fwd_masked(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const unsigned int* mask,
+                            long long mask_batch_stride,
+                            long long mask_head_stride, int B, int H, int Hkv,
+                            int Nq, int Nk, int d, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !mask) return FA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (H % Hkv != 0 || !isfinite(scale) || mask_batch_stride < 0 ||
+      mask_head_stride < 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (d != 128 || Nk > fa::MASK_MAX_NK) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(mask) & 3u))
+    return FA_ERR_MISALIGNED;
+  fa::MaskArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.mask = mask;
+  a.mask_bs = mask_batch_stride;
+  a.mask_hs = mask_head_stride;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.group = H / Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.c = scale * 1.4426950408889634f;
+  return hip_status(
+      fa::launch_masked_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,

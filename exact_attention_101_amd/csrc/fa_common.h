@@ -96,6 +96,25 @@ struct VarlenArgs {
   float c;                // scale * log2(e), signed
 };
 
+// Forward under an arbitrary visibility bit mask.
+struct MaskArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const uint32_t* mask;   // bit j % 32 of word j / 32 of a row: key j visible
+  long long mask_bs;      // words between batches' masks (0: shared)
+  long long mask_hs;      // words between query heads' masks (0: shared)
+  int B, H, Hkv;
+  int group;              // H / Hkv
+  int Nq, Nk;
+  int W;                  // words per mask row, ceil(Nk / 32)
+  int nqb;                // 128-row query blocks
+  float c;                // scale * log2(e), signed
+};
+constexpr int MASK_MAX_NK = 262144;   // keys a mask may cover
+
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).
 __device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {

@@ -198,6 +198,33 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   int window_right, float scale, void* stream);
 
 /*
+ * fa_fwd_masked -- bf16 forward under an arbitrary visibility mask.  The
+ *   FlashAttention-3 summary (GeekNews), section «Comentários no Hacker
+ *   News», reports FlashAttention being much slower with arbitrary masks.
+ *   Query i of (batch b, query head h) sees key j iff bit j % 32 of word
+ *   mask[b * mask_batch_stride + h * mask_head_stride + i * W + j / 32] is
+ *   set, W = ceil(Nk / 32); the softmax runs over the visible keys only and
+ *   a row that sees no key gets o = 0 and lse = -inf.  Work follows the
+ *   mask: a 32-key tile is loaded and computed for a block of 128 query
+ *   rows only if one of them sees one of its keys.
+ *   q, o      device, bfloat16 [B][H][Nq][d] (q read only, o written).
+ *   k, v      device, bfloat16 [B][Hkv][Nk][d] (read only).
+ *   lse       device, float [B][H][Nq] (written, natural log).
+ *   mask      device, uint32 words, 4-byte aligned, read only; each
+ *             (b, h) slice is Nq rows of W words.  Bits past Nk are ignored.
+ *   mask_batch_stride, mask_head_stride  in words, >= 0; 0 shares one mask
+ *             slice across batches or heads.
+ *   Nk at most 262144 (FA_ERR_UNSUPPORTED above); d must be 128; H, Hkv,
+ *   scale as for fa_fwd.  Errors as for fa_fwd; lse needs 4-byte alignment.
+ *   One kernel is enqueued on `stream`.
+ */
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const unsigned int* mask,
+                  long long mask_batch_stride, long long mask_head_stride,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                  void* stream);
+
+/*
  * fa_fp8_quantize -- optional random-sign Hadamard rotation of each row, then
  * per-tensor OCP e4m3 quantisation ("incoherent processing" of the
  * FlashAttention-3 summary, section «Baixa precisão: redução do erro de

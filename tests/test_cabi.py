@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv",
-              "fa_fwd_varlen",
+              "fa_fwd_varlen", "fa_fwd_masked",
               "fa_splitkv_num_splits", "fa_fp8_quantize",
               "fa_status_string",
               "fa_last_hip_error", "fa_version"):
@@ -182,3 +182,25 @@ def test_varlen_only_d128_and_alignment(lib):
     assert _vl(lib, d=64) == fa.FA_ERR_UNSUPPORTED
     assert _vl(lib, q=M) == fa.FA_ERR_MISALIGNED
     assert _vl(lib, cq=A + 2) == fa.FA_ERR_MISALIGNED
+
+
+def _mk(lib, q=A, k=A, v=A, o=A, lse=A, mask=A, mbs=0, mhs=0, B=2, H=4,
+        Hkv=2, Nq=100, Nk=120, d=128, scale=0.1):
+    return lib.fa_fwd_masked(q, k, v, o, lse, mask, mbs, mhs, B, H, Hkv, Nq,
+                             Nk, d, scale, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(mask=None), dict(B=0),
+                                dict(Nq=0), dict(Nk=0), dict(H=6, Hkv=4),
+                                dict(mbs=-1), dict(mhs=-3),
+                                dict(scale=float("inf"))])
+def test_masked_invalid_arguments(lib, kw):
+    assert _mk(lib, **kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_masked_unsupported_and_alignment(lib):
+    assert _mk(lib, d=64) == fa.FA_ERR_UNSUPPORTED
+    assert _mk(lib, Nk=262145) == fa.FA_ERR_UNSUPPORTED
+    assert _mk(lib, Nk=262144, q=M) == fa.FA_ERR_MISALIGNED
+    assert _mk(lib, mask=A + 2) == fa.FA_ERR_MISALIGNED
+    assert _mk(lib, lse=A + 1) == fa.FA_ERR_MISALIGNED
