@@ -130,6 +130,10 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
       issue(tn, kn, vn);
       mw_next = mrow[tn];
     }
+    // Keys past Nk are hidden whatever the mask says (their rows read as
+    // zeros): clear their bits once per tile instead of testing every key.
+    const int kin = Nk - t * T;
+    if (kin < T) mw &= (1u << kin) - 1u;
     const int k0 = t * T;
     f32x16_t sc = f32x16_t{};
 #pragma unroll
@@ -140,14 +144,22 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int kx = 16 * (x >> 3) + (x & 7);
-      const bool ok = ((mh >> kx) & 1u) && k0 + kx + 8 * h < Nk;
-      sc[x] = ok ? sc[x] * a.c : -__builtin_inff();
+      sc[x] = ((mh >> kx) & 1u) ? sc[x] * a.c : -__builtin_inff();
       mx = fmaxf(mx, sc[x]);
     }
     mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    // O and l are rescaled only when some row's maximum grew in this tile
+    // (alpha = 1 for every row otherwise); the test is wave-uniform.
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    }
     m = m_new;
     float p[16];
     float sum = 0.f;
@@ -156,11 +168,7 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
       p[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
       sum += p[x];
     }
-    l = l * alpha + sum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    l += sum;
     bf16x8_t pb[2];
     pack_b(p, pb);
 #pragma unroll

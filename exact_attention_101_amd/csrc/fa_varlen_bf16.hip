@@ -93,6 +93,9 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
 
   const int qi = iw0 + li;                   // this lane's query row
   const bool qok = qi < Nq;
+  // Keys this lane's row sees: [jlo, jhi] (empty for rows past Nq).
+  const int jlo = key_lo(qi);
+  const int jhi = qok ? key_hi(qi) : -1;
   const int64_t qrow = static_cast<int64_t>(hq) * a.total_q + q_beg + qi;
   bf16x8_t qf[8];
   load_row_b(static_cast<const uint16_t*>(a.q) +
@@ -132,19 +135,30 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
+    // This lane's visible keys [jlo, jhi], relative to its first key of the
+    // tile: score x (key k0 + 8 h + kx) is kept iff rlo <= kx <= rhi.
+    const int rlo = jlo - k0 - 8 * h;
+    const int rhi = jhi - k0 - 8 * h;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int j = k0 + 16 * (x >> 3) + 8 * h + (x & 7);
-      const bool ok = qok && j < Nk && (wl < 0 || j >= qi + off - wl) &&
-                      (wr < 0 || j <= qi + off + wr);
-      sc[x] = ok ? sc[x] * a.c : -__builtin_inff();
+      const int kx = 16 * (x >> 3) + (x & 7);
+      sc[x] = (kx >= rlo && kx <= rhi) ? sc[x] * a.c : -__builtin_inff();
       mx = fmaxf(mx, sc[x]);
     }
     mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    // O and l are rescaled only when some row's maximum grew in this tile
+    // (alpha = 1 for every row otherwise); the test is wave-uniform.
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    }
     m = m_new;
     float p[16];
     float sum = 0.f;
@@ -153,11 +167,7 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
       p[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
       sum += p[x];
     }
-    l = l * alpha + sum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    l += sum;
     bf16x8_t pb[2];
     pack_b(p, pb);
 #pragma unroll
