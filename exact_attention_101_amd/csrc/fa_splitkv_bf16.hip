@@ -141,6 +141,8 @@ splitkv_kernel(const SplitArgs a) {
   int kb0 = static_cast<int>(static_cast<long long>(s) * nkb / a.splits);
   int kb1 = static_cast<int>(static_cast<long long>(s + 1) * nkb / a.splits);
   const int off = Nk - Nq;                   // bottom-right causal offset
+  // This lane's last visible key (-1: none; rows past the block see none).
+  const int jhi = !rok ? -1 : (CAUSAL ? min(Nk - 1, qi + off) : Nk - 1);
   if (CAUSAL) {
     const int r_last = min(rows, rb * T + T) - 1;
     const int last_key = r_last / a.group + off;   // max over the block
@@ -207,18 +209,29 @@ splitkv_kernel(const SplitArgs a) {
     for (int t = 0; t < 8; ++t)
       sc = mfma(as_bf16x8(kt[swz(sigma(li), 8 * h + t)]), qf[t], sc);
     // Scale, mask; lane half h holds keys 16 (x / 8) + 8 h + x % 8.
+    // Score x is key kb T + 8 h + kx: kept iff kx <= rhi (this lane's last
+    // visible key, relative to its first key of the tile).
+    const int rhi = jhi - kb * T - 8 * h;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int key = kb * T + 16 * (x >> 3) + 8 * h + (x & 7);
-      const bool ok = rok && key < Nk && (!CAUSAL || key <= qi + off);
-      sc[x] = ok ? sc[x] * a.c : -__builtin_inff();
+      const int kx = 16 * (x >> 3) + (x & 7);
+      sc[x] = (kx <= rhi) ? sc[x] * a.c : -__builtin_inff();
       mx = fmaxf(mx, sc[x]);
     }
     mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);   // 0 at start
+    // O and l are rescaled only when some row's maximum grew in this tile
+    // (alpha = 1 for every row otherwise); the test is wave-uniform.
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    }
     m = m_new;
     float pr[16];
     float sum = 0.f;
@@ -227,11 +240,7 @@ splitkv_kernel(const SplitArgs a) {
       pr[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
       sum += pr[x];
     }
-    l = l * alpha + sum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+    l += sum;
     bf16x8_t pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
