@@ -132,3 +132,21 @@ def test_masked_signed_scale_and_determinism():
     _compare(o, lse, ro, rl, "scale -0.07")
     o2, lse2 = _run(tb, m, scale=-0.07)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_masked_maximum_keys_sparse():
+    """Nk = 262144, the largest the mask path takes (its tile bitmap then
+    fills all of its LDS words): a sparse mask whose visible keys include
+    the first and the last key, every row compared."""
+    B, H, Hkv, Nq, Nk = 1, 2, 1, 200, 262144
+    tb, vals = _inputs(B, H, Hkv, Nq, Nk, 7700)
+    rng = np.random.Generator(np.random.PCG64(7701))
+    m = np.zeros((1, 1, Nq, Nk), dtype=bool)
+    for i in range(Nq):
+        m[0, 0, i, rng.choice(Nk, size=40, replace=False)] = True
+    m[0, 0, :50, 0] = True
+    m[0, 0, 50:100, Nk - 1] = True
+    m[0, 0, 7, :] = False                    # a row that sees nothing
+    o, lse = _run(tb, m)
+    ro, rl = oracle.attention_masked(*vals, m)
+    _compare(o, lse, ro, rl, "Nk 262144 sparse")

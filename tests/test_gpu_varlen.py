@@ -110,3 +110,24 @@ def test_varlen_deterministic():
     a = _run(packed, LENS, True, (50, -1))
     b = _run(packed, LENS, True, (50, -1))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_varlen_long_sequence_narrow_window_sampled():
+    """One 131072-token sequence beside a short one, a 512-key causal
+    window: sampled rows, each against the oracle on its own window."""
+    lens = [(131072, 131072), (100, 100)]
+    packed, (qs, ks, vs) = _packed(lens, 2, 1, 6400)
+    o, lse = _run(packed, lens, True, (512, -1))
+    cq = packed[3]
+    for i in (0, 511, 512, 513, 70000, 131071):
+        lo = max(0, i - 512)
+        (o1,), (l1,) = oracle.attention_varlen(
+            [qs[0][:, i:i + 1]], [ks[0][:, lo:i + 1]], [vs[0][:, lo:i + 1]],
+            causal=True)
+        assert np.abs(o[:, cq[0] + i] - o1[:, 0]).max() <= BF16_O_TOL
+        assert np.abs(lse[:, cq[0] + i] - l1[:, 0]).max() <= LSE_TOL
+    (o2,), (l2,) = oracle.attention_varlen([qs[1]], [ks[1]], [vs[1]],
+                                           causal=True, window_left=512)
+    assert np.abs(o[:, cq[1]:cq[2]] - o2).max() <= BF16_O_TOL
+    assert np.abs(lse[:, cq[1]:cq[2]] - l2).max() <= LSE_TOL
+    print("131072-token sequence, window 512: sampled rows ok")
