@@ -15,6 +15,7 @@ hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
+hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream);
 hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream);
 hipError_t launch_masked_bf16(MaskArgs a, hipStream_t stream);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
@@ -213,26 +214,42 @@ FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v,
       (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
     return FA_ERR_MISALIGNED;
-  fa::VarlenArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
+  const int right = causal ? 0 : window_right;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Windows bounded on both sides and narrower than VARLEN_NARROW keys go
+  // to the 128-row kernel, whose waves skip the tiles outside their own
+  // rows' windows; everything else to the pipelined forward kernel, whose
+  // 256-row workgroups stream W + 256 keys for a window of W.
+  if (window_left >= 0 && right >= 0 &&
+      window_left + right < fa::VARLEN_NARROW) {
+    fa::VarlenArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.group = H / Hkv;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    a.max_q = max_seqlen_q;
+    a.left = window_left;
+    a.right = right;
+    a.c = scale * 1.4426950408889634f;
+    return hip_status(fa::launch_varlen_bf16(a, st));
+  }
+  fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Hkv, 0, scale);
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
-  a.B = B;
-  a.H = H;
-  a.Hkv = Hkv;
-  a.group = H / Hkv;
   a.total_q = total_q;
   a.total_k = total_k;
-  a.max_q = max_seqlen_q;
   a.left = window_left;
-  a.right = causal ? 0 : window_right;
-  a.c = scale * 1.4426950408889634f;
-  return hip_status(
-      fa::launch_varlen_bf16(a, static_cast<hipStream_t>(stream)));
+  a.right = right;
+  return hip_status(fa::launch_fwd_varlen_bf16(a, max_seqlen_q, st));
 }
 
 FA_EXPORT int fa_fwd_masked(const void* q, const void* k, const void* v,

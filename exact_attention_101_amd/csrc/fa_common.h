@@ -28,6 +28,13 @@ struct FwdArgs {
   float scale;            // signed scale (fp8 path folds descales into it)
   int neg;                // scale < 0: Q is negated on load so that c >= 0
   int xcd_chunk;          // 1: map workgroups to XCD-contiguous work ranges
+  // Variable-length / windowed launches only (unused otherwise): sequence b
+  // owns query rows [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1])
+  // of tensors packed per head; window widths (-1 = unbounded).
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int left, right;
 };
 
 // Arguments of one backward pass (bf16, d = 128).  ws holds, per query row
@@ -114,6 +121,9 @@ struct MaskArgs {
   float c;                // scale * log2(e), signed
 };
 constexpr int MASK_MAX_NK = 262144;   // keys a mask may cover
+// Variable-length windows with left + right below this many keys (both
+// bounded) run on the 128-row kernel, wider ones on the pipelined kernel.
+constexpr int VARLEN_NARROW = 512;
 
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).

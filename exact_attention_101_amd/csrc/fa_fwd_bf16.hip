@@ -56,7 +56,15 @@
 //     its exact row maximum, so the common path computes no maximum at all;
 //   * LDS layouts are chosen so every MFMA operand read is free of bank
 //     conflicts: K rows are padded by one 16-byte slot, V rows XOR their
-//     64-byte segments with the key's position in its group of 4.
+//     64-byte segments with the key's position in its group of 4;
+//   * VL (variable-length batches and sliding windows, FlashAttention-3
+//     summary, section «Comentários no Hacker News»): the causal
+//     configuration with per-sequence row offsets, a key range [lo, hi]
+//     per workgroup (tiles before lo are never loaded; K / V are addressed
+//     from lo's tile), window masks in the masked blocks, and the XCDs fed
+//     by KV head rather than by sequence.  A row that has seen no key keeps
+//     m = -inf and forms P against 0; the first block in which it sees a
+//     key takes the exact step.
 #include "fa_common.h"
 
 namespace fa {
@@ -196,7 +204,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
       soffset, 0, 0);
 }
 
-template <int D, bool CAUSAL, int NQB>
+template <int D, bool CAUSAL, int NQB, bool VL = false>
 __global__ void __launch_bounds__(Waves<NQB>::NTHR, 1)
 fwd_bf16_kernel(const FwdArgs a) {
   constexpr int NWAVE = Waves<NQB>::NWAVE;
@@ -214,22 +222,86 @@ fwd_bf16_kernel(const FwdArgs a) {
   const int h = lane >> 5;              // lane half
 
   int bh, qblk;
-  map_work(blockIdx.x, gridDim.x, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh,
-           qblk);
+  if constexpr (VL) {
+    // Sequences differ in length, so no XCD may own whole sequences:
+    // workgroups go to the 8 XCDs in turn, and XCD x takes the KV heads
+    // hk = x (mod 8) of every sequence (its query heads together, sharing
+    // K and V in that XCD's L2), longest-running query blocks first.  With
+    // Hkv not a multiple of 8, consecutive workgroups take consecutive
+    // (sequence, head) pairs.
+    const int L = blockIdx.x;
+    if (a.xcd_chunk) {
+      const int x = L & 7;
+      int t = L >> 3;
+      const int g = t % a.group;
+      t /= a.group;
+      const int hpx = a.Hkv >> 3;
+      const int hk_l = t % hpx;
+      t /= hpx;
+      const int bb = t % a.B;
+      qblk = a.nqb - 1 - t / a.B;
+      bh = bb * a.H + (hk_l * 8 + x) * a.group + g;
+    } else {
+      bh = L % (a.B * a.H);
+      qblk = a.nqb - 1 - L / (a.B * a.H);
+    }
+  } else {
+    map_work(blockIdx.x, gridDim.x, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh,
+             qblk);
+  }
   const int b = bh / a.H;
   const int hq = bh % a.H;
   const int hk = hq / a.group;
-  const int N = a.N;
   const int q0 = qblk * BR;
   const int qw0 = q0 + wave * QPW;      // first query row of this wave
   // This lane's query rows: qw0 + 32 j + li for query block j < NQB.
 
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                       (static_cast<int64_t>(b) * a.H + hq) * N * D;
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) +
-                       (static_cast<int64_t>(b) * a.Hkv + hk) * N * D;
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) +
-                       (static_cast<int64_t>(b) * a.Hkv + hk) * N * D;
+  // NQ query rows and NK keys in this (batch, head), or in this sequence of
+  // a variable-length batch: rows of Q / O start at row qrow0 of the
+  // tensor, rows of K / V at krow0.  VL: query i sees key j iff
+  // (wl < 0 or j >= i + off - wl) and (wr < 0 or j <= i + off + wr), with
+  // off = NK - NQ (bottom-right alignment).
+  int NQ, NK, off = 0, wl = -1, wr = -1;
+  int64_t qrow0, krow0;
+  if constexpr (VL) {
+    const int q_beg = a.cu_q[b];
+    const int k_beg = a.cu_k[b];
+    NQ = a.cu_q[b + 1] - q_beg;
+    NK = a.cu_k[b + 1] - k_beg;
+    // A sequence whose offsets leave the packed tensors is skipped; so are
+    // query blocks past its last row (the whole workgroup, before any
+    // barrier).
+    if (q_beg < 0 || NQ < 0 || q_beg + NQ > a.total_q || k_beg < 0 ||
+        NK < 0 || k_beg + NK > a.total_k || q0 >= NQ)
+      return;
+    off = NK - NQ;
+    wl = a.left;
+    wr = a.right;
+    qrow0 = static_cast<int64_t>(hq) * a.total_q + q_beg;
+    krow0 = static_cast<int64_t>(hk) * a.total_k + k_beg;
+  } else {
+    NQ = NK = a.N;
+    qrow0 = (static_cast<int64_t>(b) * a.H + hq) * a.N;
+    krow0 = (static_cast<int64_t>(b) * a.Hkv + hk) * a.N;
+  }
+  // Keys [kv_begin, kv_begin + kv_end) are streamed (kv_begin is a multiple
+  // of BT); blocks and tiles below count from kv_begin.
+  int kv_begin = 0, kv_end;
+  if constexpr (VL) {
+    const int i1 = min(NQ, q0 + BR) - 1;
+    const int lo = wl < 0 ? 0 : max(0, q0 + off - wl);
+    const int hi = wr < 0 ? NK - 1 : min(NK - 1, i1 + off + wr);
+    kv_begin = hi < lo ? 0 : (lo / BT) * BT;
+    kv_end = hi < lo ? 0 : hi + 1 - kv_begin;
+  } else {
+    kv_end = CAUSAL ? min(NK, q0 + BR) : NK;   // last key needed + 1
+  }
+
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow0 * D;
+  const uint16_t* kp =
+      static_cast<const uint16_t*>(a.k) + (krow0 + kv_begin) * D;
+  const uint16_t* vp =
+      static_cast<const uint16_t*>(a.v) + (krow0 + kv_begin) * D;
 
   // ---- Q -> registers (B operand of S^T = K Q^T), NQB query blocks ----
   bf16x8_t qf[NQB][G::NKS];
@@ -238,8 +310,8 @@ fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       const int row = qw0 + 32 * j + li;
-      const bool ok = row < N;
-      const uint16_t* src = qp + static_cast<int64_t>(ok ? row : N - 1) * D +
+      const bool ok = row < NQ;
+      const uint16_t* src = qp + static_cast<int64_t>(ok ? row : NQ - 1) * D +
                             h * (D / 2);
 #pragma unroll
       for (int s = 0; s < G::NKS; ++s) {
@@ -297,7 +369,6 @@ fwd_bf16_kernel(const FwdArgs a) {
     return i < G::KINS / NWAVE || i < kinst;
   };
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
   const int ntiles = (kv_end + BT - 1) / BT;
   const int nblk = 2 * ntiles;          // key blocks of BC keys
   // Steps 1 .. nsteps run in rounds of four; step b ends with O += P(b-1)
@@ -382,21 +453,46 @@ fwd_bf16_kernel(const FwdArgs a) {
   // Hide the scores of keys a row may not see (causal: key > query;
   // ragged tail: key >= N) by setting them to -inf.  Lane half h holds keys
   // kv0 + 16 (r / 8) + 8 h + (r % 8) of the 32-key block.
-  auto apply_mask = [&](f32x16_t (&s)[NQB], int kv0) {
+  // VL: vis[j] says whether the row of query block j sees any key of the
+  // block (rows that have seen none so far must take the exact step on the
+  // first block where they do).
+  auto apply_mask = [&](f32x16_t (&s)[NQB], int kv0, bool (&vis)[NQB]) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       const int qrow = qw0 + 32 * j + li;
+      if constexpr (VL) {
+        // This row's visible keys [jlo, jhi], relative to the lane's first
+        // key of the block: score r (key base + kx) is kept iff
+        // rlo <= kx <= rhi.
+        const int base = kv_begin + kv0 + 8 * h;
+        const int jlo = wl < 0 ? 0 : qrow + off - wl;
+        const int jhi = wr < 0 ? NK - 1 : min(NK - 1, qrow + off + wr);
+        const int rlo = jlo - base, rhi = jhi - base;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 16 * (r >> 3) + 8 * h + (r & 7);
-        const bool ok = key < N && (!CAUSAL || key <= qrow);
-        if (!ok) s[j][r] = -__builtin_inff();
+        for (int r = 0; r < 16; ++r) {
+          const int kx = 16 * (r >> 3) + (r & 7);
+          if (!(kx >= rlo && kx <= rhi)) s[j][r] = -__builtin_inff();
+        }
+        // The lane's keys are kx in 0..7 and 16..23.
+        vis[j] = rlo <= rhi && ((rlo <= 7 && rhi >= 0) ||
+                                (rlo <= 23 && rhi >= 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool ok = key < NK && (!CAUSAL || key <= qrow);
+          if (!ok) s[j][r] = -__builtin_inff();
+        }
       }
     }
   };
   auto masked_at = [&](int blk) {
-    const int kv0 = blk * BC;
-    return (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+    const int kv0 = kv_begin + blk * BC;
+    if constexpr (VL)
+      return (kv0 + BC > NK) || (wr >= 0 && kv0 + BC - 1 > qw0 + off + wr) ||
+             (wl >= 0 && kv0 < qw0 + QPW - 1 + off - wl);
+    else
+      return (kv0 + BC > NK) || (CAUSAL && kv0 + BC - 1 > qw0);
   };
 
   // Exact step for a block whose P (formed with the held m) has a lane sum
@@ -494,6 +590,8 @@ fwd_bf16_kernel(const FwdArgs a) {
   // c > 0).  A SYNC step (odd blk) first waits for the copies issued two
   // steps earlier, then starts those of tiles (blk-1)/2 + 2 (K, into kw)
   // and (blk-1)/2 + 1 (V, into vw).
+  // VL: whether the block now in `s` holds a key each row sees.
+  bool svis[NQB];
   auto step = [&](int blk, f32x16_t (&s)[NQB], bf16x8_t (&pp)[NQB][2],
                   const uint4* kr, const uint4* vr, const uint4* kw,
                   const uint4* vw, auto kh_tag, auto vh_tag, auto sync_tag,
@@ -512,7 +610,16 @@ fwd_bf16_kernel(const FwdArgs a) {
     if constexpr (SYNC) wait_copies_and_sync();
     float mu[NQB];
 #pragma unroll
-    for (int j = 0; j < NQB; ++j) mu[j] = m_run[j];
+    for (int j = 0; j < NQB; ++j) {
+      // VL: a row that has seen no key yet (m = -inf) forms P against 0, so
+      // that fully masked blocks give p = 0 instead of NaN; the first block
+      // in which it sees a key takes the exact step (sum test below), which
+      // sets m from that block.
+      if constexpr (VL)
+        mu[j] = (m_run[j] == -__builtin_inff()) ? 0.f : m_run[j];
+      else
+        mu[j] = m_run[j];
+    }
     uint4 kf[KPF];
     i16x4_t vf[VPF][2];
     if constexpr (QK) {
@@ -600,6 +707,8 @@ fwd_bf16_kernel(const FwdArgs a) {
     for (int j = 0; j < NQB; ++j) {
       ls[j] = lse_[j] + lso_[j];
       bad = bad || !(ls[j] <= TAU_EXP2);
+      if constexpr (VL)
+        bad = bad || (m_run[j] == -__builtin_inff() && svis[j]);
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0) exact_block(s, w, ls);  // rare
 #pragma unroll
@@ -613,9 +722,16 @@ fwd_bf16_kernel(const FwdArgs a) {
             make_uint4(w[8 * j + 4 * u], w[8 * j + 4 * u + 1],
                        w[8 * j + 4 * u + 2], w[8 * j + 4 * u + 3]));
     if constexpr (QK) {
-      if (masked_at(blk + 1)) apply_mask(sn, (blk + 1) * BC);
+      bool vn[NQB];
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) vn[j] = true;
+      if (masked_at(blk + 1)) apply_mask(sn, (blk + 1) * BC, vn);
 #pragma unroll
       for (int j = 0; j < NQB; ++j) s[j] = sn[j];
+      if constexpr (VL) {
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) svis[j] = vn[j];
+      }
     }
   };
 
@@ -639,9 +755,12 @@ fwd_bf16_kernel(const FwdArgs a) {
     s[i % NQB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         as_bf16x8(kfrag(Ks0, 0, i / NQB)), qf[i % NQB][i / NQB], s[i % NQB],
         0, 0, 0);
-  if (masked_at(0)) apply_mask(s, 0);
-  // Reference max from block 0 (every row sees key 0, so m is finite for
-  // the rows that exist).
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) svis[j] = true;
+  if (masked_at(0)) apply_mask(s, 0, svis);
+  // Reference max from block 0 (without VL every row sees key 0, so m is
+  // finite for the rows that exist; with VL a row may see nothing yet and
+  // keep m = -inf).
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     float mx = s[j][0];
@@ -670,9 +789,8 @@ fwd_bf16_kernel(const FwdArgs a) {
     const int qrow = qw0 + 32 * j + li;
     const float l_tot = half_sum(l_run[j]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-      uint16_t* op = static_cast<uint16_t*>(a.o) +
-                     ((static_cast<int64_t>(b) * a.H + hq) * N + qrow) * D;
+    if (qrow < NQ) {
+      uint16_t* op = static_cast<uint16_t*>(a.o) + (qrow0 + qrow) * D;
       // Accumulator row m <-> d = 32 db + sigma(m): lane half h holds
       // d = 32 db + 16 u + 8 h + (0..7) in registers 8 u .. 8 u + 7.
 #pragma unroll
@@ -690,7 +808,7 @@ fwd_bf16_kernel(const FwdArgs a) {
       }
       if (h == 0) {
         const float m_fin = (m_run[j] == -__builtin_inff()) ? 0.f : m_run[j];
-        float* lp = a.lse + (static_cast<int64_t>(b) * a.H + hq) * N + qrow;
+        float* lp = a.lse + qrow0 + qrow;
         *lp = (l_tot > 0.f) ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f
                             : -__builtin_inff();
       }
@@ -709,6 +827,21 @@ static hipError_t launch(const FwdArgs& a, int grid, hipStream_t stream) {
   constexpr int NQB = CAUSAL ? 1 : 2;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NQB>), dim3(grid),
                      dim3(Waves<NQB>::NTHR), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Variable-length batches and sliding windows (d = 128): the causal
+// configuration (8 waves of 32 rows) with per-sequence offsets and window
+// masks.  a.nqb covers the longest query sequence.
+hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream) {
+  a.nqb = (max_q + BR - 1) / BR;
+  const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  if (static_cast<long long>(a.total_k) * 128 * 2 > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
+  a.xcd_chunk = a.Hkv % 8 == 0;
+  hipLaunchKernelGGL((fwd_bf16_kernel<128, true, 1, true>), dim3((int)grid),
+                     dim3(Waves<1>::NTHR), 0, stream, a);
   return hipGetLastError();
 }
 

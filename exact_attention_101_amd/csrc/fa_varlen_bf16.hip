@@ -1,5 +1,8 @@
 // Masked forward (bf16, d = 128) for gfx950 (MI355X): variable-length
-// batches and sliding windows.
+// batches with narrow sliding windows.  fa_fwd_varlen sends windows bounded
+// on both sides and narrower than VARLEN_NARROW keys here; wider and
+// unbounded ones run on the pipelined forward kernel (fa_fwd_bf16.hip),
+// whose 256-row workgroups would stream W + 256 keys for a window of W.
 //
 // The FlashAttention-3 summary (GeekNews), section «Comentários no Hacker
 // News», asks why FlashAttention is much slower with variable masking and

@@ -131,3 +131,35 @@ def test_varlen_long_sequence_narrow_window_sampled():
     assert np.abs(o[:, cq[1]:cq[2]] - o2).max() <= BF16_O_TOL
     assert np.abs(lse[:, cq[1]:cq[2]] - l2).max() <= LSE_TOL
     print("131072-token sequence, window 512: sampled rows ok")
+
+
+@pytest.mark.parametrize("causal,window", [(True, (300, -1)),
+                                           (False, (100, 50)),
+                                           (True, (700, -1)),
+                                           (False, (400, 200))])
+def test_varlen_window_large_scores(causal, window):
+    """Windows whose rows first see a key several blocks into their
+    workgroup's key range, with scores large enough that blocks often pass
+    the pipelined kernel's sum test: every row against the oracle.  Widths
+    below 512 run on the 128-row kernel, the others on the pipelined one."""
+    lens = [(1500, 1500), (700, 900)]
+    packed, vals = _packed(lens, 4, 2, 6500)
+    o, lse = _run(packed, lens, causal, window, scale=0.35)
+    ro, rl = oracle.attention_varlen(*vals, causal=causal,
+                                     window_left=window[0],
+                                     window_right=window[1], scale=0.35)
+    _check(o, lse, ro, rl, packed[3], f"scale 0.35 window={window}")
+
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (64, -1)),
+                                           (False, (40, 7)), (True, (600, -1)),
+                                           (False, (300, 300))])
+def test_varlen_kv_heads_multiple_of_8(causal, window):
+    """16 query heads on 8 KV heads: the launch then spreads each KV head's
+    work over the XCDs by head, not by sequence."""
+    packed, vals = _packed(LENS, 16, 8, 6600)
+    o, lse = _run(packed, LENS, causal, window)
+    ro, rl = oracle.attention_varlen(*vals, causal=causal,
+                                     window_left=window[0],
+                                     window_right=window[1])
+    _check(o, lse, ro, rl, packed[3], f"Hkv 8 causal={causal} window={window}")
