@@ -87,6 +87,12 @@ def _time_launches(fn, steps: int, warmup: int):
             "min": each[0]}
 
 
+def _progress(msg: str) -> None:
+    """One line on stderr per finished measurement (stdout carries only the
+    JSON result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def _bf16_workload(name):
     """Seeded inputs of a named bf16 workload: device bf16 tensors plus the
     host bf16 tensors they were copied from."""
@@ -190,6 +196,7 @@ def main() -> int:
     head = _time_launches(step, args.steps, args.warmup)
     ms = head["mean"]
     tflops = w.flops / (ms * 1e-3) / 1e12
+    _progress(f"{w.name}: {ms:.4f} ms, {tflops:.1f} TFLOP/s")
 
     extras = {}
     if not args.no_extras:
@@ -206,6 +213,7 @@ def main() -> int:
             extras[name] = {"ms": round(m, 4), "ms_median": round(tm["median"], 4),
                             "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                             "frac_of_bf16_peak": round(t / BF16_PEAK_TFLOPS, 4)}
+            _progress(f"{name}: {extras[name]}")
             del qq, kk, vv, oo, ll
         # Backward of the headline workload (dQ, dK, dV from the forward's O
         # and LSE and a seeded dO).  Throughput counts 2.5x the forward's
@@ -226,6 +234,7 @@ def main() -> int:
             "ms_min": round(tm_b["min"], 4), "TFLOP/s": round(tb, 1),
             "frac_of_bf16_peak": round(tb / BF16_PEAK_TFLOPS, 4),
             "flops": "2.5 x forward (10 B H N^2 d)"}
+        _progress(f"bf16_n8192_backward: {extras['bf16_n8192_backward']}")
         del dout, dq, dk, dv, ws
         # Decode at long context through the split-KV forward: one query
         # per head, 32 query heads on 8 KV heads, 65536 keys, B = 8.  Bound
@@ -249,6 +258,7 @@ def main() -> int:
             "ms_min": round(tm_d["min"], 4), "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "num_splits": ns, "bytes": "K and V once"}
+        _progress(f"decode_b8_h32_hkv8_nk65536: {extras['decode_b8_h32_hkv8_nk65536']}")
         del qd, kd, vd, od, ld, wd
         # Variable-length batch with a causal sliding window (4096 keys to the
         # left): 8 sequences of 2K..16K tokens, 32 query heads on 8 KV heads.
@@ -275,6 +285,7 @@ def main() -> int:
             "ms_min": round(tm_v["min"], 4), "TFLOP/s": round(tvl, 1),
             "frac_of_bf16_peak": round(tvl / BF16_PEAK_TFLOPS, 4),
             "flops": "4 d per visible (query, key) pair"}
+        _progress(f"varlen_causal_window4096: {extras['varlen_causal_window4096']}")
         del qv_, kv_, vv_, ov_, lv_
         # Arbitrary masks on the headline shape (B4 H16 N8192 d128), one
         # mask shared by every (batch, head): a block-sparse pattern of
@@ -301,6 +312,7 @@ def main() -> int:
                 "frac_of_bf16_peak": round(tmk / BF16_PEAK_TFLOPS, 4),
                 "visible_fraction": round(vis / float(w.N) ** 2, 4),
                 "flops": "4 d per visible (query, key) pair"}
+            _progress(f"{mname}: {extras[mname]}")
             del mw_
         ww = workloads.WORKLOADS["fp8_n8192"]
         xq, xk, xv = (torch.from_numpy(x).to(dev)
@@ -324,11 +336,13 @@ def main() -> int:
             extras[key] = {"ms": round(m, 4), "ms_median": round(tm["median"], 4),
                            "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
+            _progress(f"{key}: {extras[key]}")
         mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20)["mean"]
         nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
         extras["fp8_quantize_hadamard_per_tensor"] = {
             "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        _progress(f"fp8_quantize_hadamard_per_tensor: {extras['fp8_quantize_hadamard_per_tensor']}")
         del xq, xk, xv, q8, k8, v8, oo, ll
         # Context, not part of the path: the vendor bf16 GEMM (hipBLASLt via
         # torch.matmul) on N(0,1) operands of the same distribution, i.e. what
@@ -343,6 +357,7 @@ def main() -> int:
         extras["library_gemm_bf16_8192_randn"] = {
             "ms": round(mg, 4), "TFLOP/s": round(tg, 1),
             "frac_of_bf16_peak": round(tg / BF16_PEAK_TFLOPS, 4)}
+        _progress(f"library_gemm_bf16_8192_randn: {extras['library_gemm_bf16_8192_randn']}")
         del a, bt, c
 
     cpu = None
