@@ -134,11 +134,10 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
     // zeros): clear their bits once per tile instead of testing every key.
     const int kin = Nk - t * T;
     if (kin < T) mw &= (1u << kin) - 1u;
-    const int k0 = t * T;
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
-    // Lane half h holds keys k0 + 16 (x / 8) + 8 h + x % 8.
+    // Lane half h holds keys t T + 16 (x / 8) + 8 h + x % 8.
     const uint32_t mh = qok ? (mw >> (8 * h)) : 0u;
     float mx = -__builtin_inff();
 #pragma unroll
