@@ -579,7 +579,9 @@ fwd_bf16_kernel(const FwdArgs a) {
     mfma_pv_acc(v8, pb, acc);
   };
 
-  static_assert(NCOPY <= NSL, "one copy per issue slot");
+  static_assert(NCOPY + 1 <= NSL, "one copy per issue slot after the first");
+  static_assert(G::NKS - KPF == NVF - VPF,
+                "K and V read-ahead cross into the next step in one slot");
   // Step blk of the three-stage pipeline.  On entry `s` holds the (masked)
   // scores of block blk and `pp` the settled P of block blk-1.  The K stage
   // kr (32-key half KH) holds block blk+1, the V stage vr (half VH) block
@@ -587,27 +589,38 @@ fwd_bf16_kernel(const FwdArgs a) {
   // (QK) and one MFMA of O += P(blk-1) V(blk-1) (PV) with PPS score pairs
   // of block blk turned into P (p = exp2(S c - m), fp32 lane sums, bf16
   // pack).  Masked scores are -inf and give p = 0 (the launcher keeps
-  // c > 0).  A SYNC step (odd blk) first waits for the copies issued two
-  // steps earlier, then starts those of tiles (blk-1)/2 + 2 (K, into kw)
-  // and (blk-1)/2 + 1 (V, into vw).
+  // c > 0).  A SYNC step (odd blk) starts the copies of tiles (blk-1)/2 + 2
+  // (K, into kw) and (blk-1)/2 + 1 (V, into vw).
+  // K and V fragments are read KPF / VPF fragments ahead of their MFMA, and
+  // the read-ahead runs on into the next step (stages krn / vrn, halves
+  // KHN / VHN), so a step starts with its first operands in registers: on
+  // entry kf / vf hold this step's first KPF / VPF fragments.  When the
+  // next step is a SYNC step, its stages were just filled by copies, and
+  // the stages this step reads are the ones the next step's copies
+  // overwrite: before the first read of the next stage, every wave waits
+  // for its own reads and copies and meets the others at the barrier.
   // VL: whether the block now in `s` holds a key each row sees.
   bool svis[NQB];
   auto step = [&](int blk, f32x16_t (&s)[NQB], bf16x8_t (&pp)[NQB][2],
+                  uint4 (&kf)[KPF], i16x4_t (&vf)[VPF][2],
                   const uint4* kr, const uint4* vr, const uint4* kw,
-                  const uint4* vw, auto kh_tag, auto vh_tag, auto sync_tag,
-                  auto pv_tag) {
+                  const uint4* vw, const uint4* krn, const uint4* vrn,
+                  auto kh_tag, auto vh_tag, auto khn_tag, auto vhn_tag,
+                  auto sync_tag, auto pv_tag, auto nsync_tag) {
     constexpr int KH = decltype(kh_tag)::value;
     constexpr int VH = decltype(vh_tag)::value;
+    constexpr int KHN = decltype(khn_tag)::value;
+    constexpr int VHN = decltype(vhn_tag)::value;
     constexpr bool SYNC = decltype(sync_tag)::value;
     constexpr bool QK = true;
     constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool NSYNC = decltype(nsync_tag)::value;
     // SYNC steps start the copies of tiles (blk-1)/2 + 2 (K, into kw) and
-    // (blk-1)/2 + 1 (V, into vw), one per issue slot, so that their issue
-    // overlaps the matrix work.
+    // (blk-1)/2 + 1 (V, into vw), one per issue slot from slot 1 on, so
+    // that their issue overlaps the matrix work; their descriptors are
+    // formed after the first MFMA has been issued.
     const int tile = (blk - 1) >> 1;
-    const auto rk = rsrc_at(kp, (tile + 2) * BT);
-    const auto rv = rsrc_at(vp, (tile + 1) * BT);
-    if constexpr (SYNC) wait_copies_and_sync();
+    __amdgpu_buffer_rsrc_t rk, rv;
     float mu[NQB];
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
@@ -619,19 +632,6 @@ fwd_bf16_kernel(const FwdArgs a) {
         mu[j] = (m_run[j] == -__builtin_inff()) ? 0.f : m_run[j];
       else
         mu[j] = m_run[j];
-    }
-    uint4 kf[KPF];
-    i16x4_t vf[VPF][2];
-    if constexpr (QK) {
-#pragma unroll
-      for (int i = 0; i < KPF; ++i) kf[i] = kfrag(kr, KH, i);
-    }
-    if constexpr (PV) {
-#pragma unroll
-      for (int i = 0; i < VPF; ++i) {
-        vf[i][0] = vread(vr, VH, i, 0);
-        vf[i][1] = vread(vr, VH, i, 1);
-      }
     }
     f32x16_t sn[NQB];
 #pragma unroll
@@ -658,9 +658,18 @@ fwd_bf16_kernel(const FwdArgs a) {
         }
         sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(kcur), qf[qb][f], sn[qb], 0, 0, 0);
+        if (qb == 0 && f + KPF >= G::NKS) {
+          // First read of the next step's stage (V's follows in this slot).
+          if (NSYNC && f + KPF == G::NKS) wait_copies_and_sync();
+          kf[f % KPF] = kfrag(krn, KHN, f + KPF - G::NKS);
+        }
       }
       if constexpr (SYNC) {
-        if (i < NCOPY) copy_nth(i, rk, rv, kw, vw);
+        if (i == 0) {
+          rk = rsrc_at(kp, (tile + 2) * BT);
+          rv = rsrc_at(vp, (tile + 1) * BT);
+        }
+        if (i >= 1 && i <= NCOPY) copy_nth(i - 1, rk, rv, kw, vw);
       }
       __builtin_amdgcn_sched_barrier(0);
       float e[PPS][2];
@@ -687,6 +696,15 @@ fwd_bf16_kernel(const FwdArgs a) {
           }
         }
         mfma_pv(vcur, pp[qb][f / G::NDB], oacc[qb][f % G::NDB]);
+      }
+      {
+        // Read-ahead into the next step, which always has a P V product
+        // (after the barrier above when the next step is a SYNC step).
+        const int f = i / NQB, qb = i % NQB;
+        if (qb == 0 && f + VPF >= NVF) {
+          vf[f % VPF][0] = vread(vrn, VHN, f + VPF - NVF, 0);
+          vf[f % VPF][1] = vread(vrn, VHN, f + VPF - NVF, 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -774,12 +792,26 @@ fwd_bf16_kernel(const FwdArgs a) {
   using T0 = Tag<false>;
   using T1 = Tag<true>;
   // ---- step 0 (no P V yet), then rounds of four steps ----
-  step(0, s, pp, Ks0, Vs1, Ks0, Vs0, Int<1>{}, Int<1>{}, T0{}, T0{});
+  // Step 0's first K fragments (block 1: stage Ks0, half 1); it has no
+  // P V product, so its V read-ahead only serves step 1.
+  uint4 kf[KPF];
+  i16x4_t vf[VPF][2] = {};
+#pragma unroll
+  for (int i = 0; i < KPF; ++i) kf[i] = kfrag(Ks0, 1, i);
+  // Arguments: K / V stages read, K / V stages written (SYNC steps), the
+  // next step's K / V stages, halves read now and next, SYNC, P V, next
+  // step SYNC.
+  step(0, s, pp, kf, vf, Ks0, Vs1, Ks0, Vs0, Ks1, Vs0, Int<1>{}, Int<1>{},
+       Int<0>{}, Int<0>{}, T0{}, T0{}, T1{});
   for (int blk = 1; blk <= nsteps; blk += 4) {
-    step(blk, s, pp, Ks1, Vs0, Ks0, Vs1, Int<0>{}, Int<0>{}, T1{}, T1{});
-    step(blk + 1, s, pp, Ks1, Vs0, Ks0, Vs1, Int<1>{}, Int<1>{}, T0{}, T1{});
-    step(blk + 2, s, pp, Ks0, Vs1, Ks1, Vs0, Int<0>{}, Int<0>{}, T1{}, T1{});
-    step(blk + 3, s, pp, Ks0, Vs1, Ks1, Vs0, Int<1>{}, Int<1>{}, T0{}, T1{});
+    step(blk, s, pp, kf, vf, Ks1, Vs0, Ks0, Vs1, Ks1, Vs0, Int<0>{},
+         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{});
+    step(blk + 1, s, pp, kf, vf, Ks1, Vs0, Ks0, Vs1, Ks0, Vs1, Int<1>{},
+         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{});
+    step(blk + 2, s, pp, kf, vf, Ks0, Vs1, Ks1, Vs0, Ks0, Vs1, Int<0>{},
+         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{});
+    step(blk + 3, s, pp, kf, vf, Ks0, Vs1, Ks1, Vs0, Ks1, Vs0, Int<1>{},
+         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{});
   }
 
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
