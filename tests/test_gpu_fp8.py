@@ -20,7 +20,7 @@ def _quant(x, signs=None):
 
 
 @pytest.mark.parametrize("rotate", [False, True])
-@pytest.mark.parametrize("rows", [1, 7, 1000, 33000])
+@pytest.mark.parametrize("rows", [1, 7, 1000, 33000, 70001])
 def test_quantize_matches_oracle(rotate, rows):
     x = workloads.draw((rows, 128), 1234 + rows, outliers=True)
     signs = workloads.hadamard_signs(128, 9) if rotate else None
