@@ -86,11 +86,12 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc,
       0);
 }
 
-// Physical chunk of (row r, logical chunk c) in a tile: the 64-byte segment
-// index is XOR-ed with r % 4 (an involution), so the 4 rows of one
-// transposing read hit 4 different bank groups.
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * NCH + ((((c >> 2) ^ (r & 3)) << 2) | (c & 3));
+// Physical chunk of (row r, logical chunk c) in a K tile: the chunk index is
+// XOR-ed with r % 16, so the 16 rows that one read phase takes at the same
+// logical chunk (rows sigma(li), a permutation of each group of 16) sit in
+// 16 different 16-byte bank groups of the 256-byte bank row.
+__device__ __forceinline__ int kswz(int r, int c) {
+  return r * NCH + (c ^ (r & 15));
 }
 
 template <bool CAUSAL>
@@ -154,14 +155,18 @@ splitkv_kernel(const SplitArgs a) {
   const char* vp = static_cast<const char*>(a.v) + khead * D * 2;
 
   // Copy j of a tile: lane writes chunk 64 j + lane = (row, physical p),
-  // whose logical chunk is the same XOR applied again.
-  uint32_t coff[TILE / 64];
+  // whose logical chunk is the same XOR applied again.  V: the 64-byte
+  // segment index is XOR-ed with row % 4, so the 4 rows of one transposing
+  // read hit 4 different bank groups; K: kswz's chunk XOR.  Each copy reads
+  // 4 whole rows.
+  uint32_t coff[TILE / 64], kcoff[TILE / 64];
 #pragma unroll
   for (int j = 0; j < TILE / 64; ++j) {
     const int slot = 64 * j + lane;
     const int rr = slot / NCH, p = slot % NCH;
     const int c = (((p >> 2) ^ (rr & 3)) << 2) | (p & 3);
     coff[j] = static_cast<uint32_t>(rr * D * 2 + c * 16);
+    kcoff[j] = static_cast<uint32_t>(rr * D * 2 + (p ^ (rr & 15)) * 16);
   }
   auto issue = [&](int kb, uint4* kd, uint4* vd) {
     const int k0 = kb * T;
@@ -174,7 +179,7 @@ splitkv_kernel(const SplitArgs a) {
         nrows * D * 2, 0x00020000);
 #pragma unroll
     for (int j = 0; j < TILE / 64; ++j) {
-      copy16(rk, kd + 64 * j, coff[j]);
+      copy16(rk, kd + 64 * j, kcoff[j]);
       copy16(rv, vd + 64 * j, coff[j]);
     }
   };
@@ -207,7 +212,7 @@ splitkv_kernel(const SplitArgs a) {
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      sc = mfma(as_bf16x8(kt[swz(sigma(li), 8 * h + t)]), qf[t], sc);
+      sc = mfma(as_bf16x8(kt[kswz(sigma(li), 8 * h + t)]), qf[t], sc);
     // Scale, mask; lane half h holds keys 16 (x / 8) + 8 h + x % 8.
     // Score x is key kb T + 8 h + kx: kept iff kx <= rhi (this lane's last
     // visible key, relative to its first key of the tile).
