@@ -637,9 +637,9 @@ fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) sn[j] = f32x16_t{};
     uint32_t w[NPR];
-    float lse_[NQB], lso_[NQB];         // lane sums of even / odd pairs
-#pragma unroll
-    for (int j = 0; j < NQB; ++j) lse_[j] = lso_[j] = 0.f;
+    // Lane sums of the even / odd pairs of each query block, started by its
+    // first two pairs (8 j and 8 j + 1).
+    float lse_[NQB], lso_[NQB];
     uint4 kcur = {};
     i16x4_t vcur[2] = {};
     __builtin_amdgcn_sched_barrier(0);
@@ -713,8 +713,12 @@ fwd_bf16_kernel(const FwdArgs a) {
         const int j = pr >> 3;
         const float p0 = e[q][0], p1 = e[q][1];
         w[pr] = pack_bf16x2(p0, p1);
-        if (pr & 1) lso_[j] += p0 + p1; else lse_[j] += p0 + p1;
-        asm volatile("" : "+v"(w[pr]), "+v"(lse_[j]), "+v"(lso_[j]));
+        float& acc = (pr & 1) ? lso_[j] : lse_[j];
+        if (pr < 8 * j + 2)
+          acc = p0 + p1;
+        else
+          acc += p0 + p1;
+        asm volatile("" : "+v"(w[pr]), "+v"(acc));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
