@@ -137,14 +137,24 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
-    // Lane half h holds keys t T + 16 (x / 8) + 8 h + x % 8.
-    const uint32_t mh = qok ? (mw >> (8 * h)) : 0u;
+    // Lane half h holds keys t T + 16 (x / 8) + 8 h + x % 8.  When every
+    // row of the wave sees every key of the tile (dense regions of a mask),
+    // the per-key tests are skipped (a wave-uniform branch).
     float mx = -__builtin_inff();
+    if (__builtin_amdgcn_ballot_w64(!(qok && mw == 0xFFFFFFFFu)) == 0) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int kx = 16 * (x >> 3) + (x & 7);
-      sc[x] = ((mh >> kx) & 1u) ? sc[x] * a.c : -__builtin_inff();
-      mx = fmaxf(mx, sc[x]);
+      for (int x = 0; x < 16; ++x) {
+        sc[x] *= a.c;
+        mx = fmaxf(mx, sc[x]);
+      }
+    } else {
+      const uint32_t mh = qok ? (mw >> (8 * h)) : 0u;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int kx = 16 * (x >> 3) + (x & 7);
+        sc[x] = ((mh >> kx) & 1u) ? sc[x] * a.c : -__builtin_inff();
+        mx = fmaxf(mx, sc[x]);
+      }
     }
     mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
