@@ -129,14 +129,25 @@ __global__ void __launch_bounds__(NTHR, 1) bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int f = 0; f < 8; ++f) dp = mfma(row_frag(vr, li, h, f), of[f], dp);
     float ds[16];
+    if (k0 + T <= N && (!CAUSAL || k0 + T - 1 <= qw0)) {
+      // Every key of the tile is visible to every row of the wave (the
+      // test is wave-uniform).  Lanes of rows past N see finite values
+      // (zero Q and dO, zero {LSE, D}) and their dQ is never stored.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
-      const bool ok = qok && key < N && (!CAUSAL || key <= qrow);
-      // exp2(-inf) = 0 masks without a branch.
-      const float p = __builtin_amdgcn_exp2f(
-          ok ? fmaf(s[r], a.c, -lse2) : -__builtin_inff());
-      ds[r] = p * (dp[r] - dq_row);
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -lse2));
+        ds[r] = p * (dp[r] - dq_row);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
+        const bool ok = qok && key < N && (!CAUSAL || key <= qrow);
+        // exp2(-inf) = 0 masks without a branch.
+        const float p = __builtin_amdgcn_exp2f(
+            ok ? fmaf(s[r], a.c, -lse2) : -__builtin_inff());
+        ds[r] = p * (dp[r] - dq_row);
+      }
     }
     bf16x8_t dsb[2];
     pack_b(ds, dsb);
