@@ -364,10 +364,13 @@ fwd_fp8_kernel(const FwdArgs a) {
     f32x16_t sn[2];
     sn[0] = f32x16_t{};
     sn[1] = f32x16_t{};
+    // Packed P words: each is written as its low half, then its high half,
+    // so its starting contents do not matter (left undefined, which spares
+    // clearing them).  The lane sums start from the first two pairs.
     int pw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pw[i] = 0;
-    float ls0 = 0.f, ls1 = 0.f;
+    for (int i = 0; i < 8; ++i) asm volatile("" : "=v"(pw[i]));
+    float ls0, ls1;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -407,8 +410,12 @@ fwd_fp8_kernel(const FwdArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int pr = 4 * i + q;
         pw[pr >> 1] = pack_fp8x2(e[q][0], e[q][1], pw[pr >> 1], pr & 1);
-        if (q & 1) ls1 += e[q][0] + e[q][1]; else ls0 += e[q][0] + e[q][1];
-        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls0), "+v"(ls1));
+        float& ls = (q & 1) ? ls1 : ls0;
+        if (pr < 2)
+          ls = e[q][0] + e[q][1];
+        else
+          ls += e[q][0] + e[q][1];
+        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
