@@ -315,17 +315,21 @@ fwd_fp8_kernel(const FwdArgs a) {
 
   // Row maximum of a tile's (masked) scores, both lane halves; -inf if
   // every key of the tile is hidden from the row.
+  // A tree of three-input maxima: 32 values -> 12 -> 4 -> 1 in 16
+  // v_maximum3_f32 (the maximum is exact, so the order is free).
   auto tile_max = [&](const f32x16_t (&s)[2]) {
-    float m[8];
+    auto at = [&](int j) { return s[j >> 4][j & 15]; };
+    float m1[12];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 4 * i;
-      m[i] = maxf(maxf(s[j >> 4][j & 15], s[(j + 1) >> 4][(j + 1) & 15]),
-                  maxf(s[(j + 2) >> 4][(j + 2) & 15],
-                       s[(j + 3) >> 4][(j + 3) & 15]));
-    }
-    const float mx = maxf(maxf(maxf(m[0], m[1]), maxf(m[2], m[3])),
-                          maxf(maxf(m[4], m[5]), maxf(m[6], m[7])));
+    for (int i = 0; i < 10; ++i)
+      m1[i] = maxf(maxf(at(3 * i), at(3 * i + 1)), at(3 * i + 2));
+    m1[10] = at(30);
+    m1[11] = at(31);
+    float m2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m2[i] = maxf(maxf(m1[3 * i], m1[3 * i + 1]), m1[3 * i + 2]);
+    const float mx = maxf(maxf(maxf(m2[0], m2[1]), m2[2]), m2[3]);
     return half_max(mx);
   };
   // E for a tile with row maximum mx (raw score): the smallest integer,
