@@ -140,14 +140,24 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
     // This lane's visible keys [jlo, jhi], relative to its first key of the
     // tile: score x (key k0 + 8 h + kx) is kept iff rlo <= kx <= rhi.
+    // When every lane sees all its keys of the tile (kx = 0..7, 16..23), a
+    // wave-uniform branch skips the per-key tests.
     const int rlo = jlo - k0 - 8 * h;
     const int rhi = jhi - k0 - 8 * h;
     float mx = -__builtin_inff();
+    if (__builtin_amdgcn_ballot_w64(!(rlo <= 0 && rhi >= 23)) == 0) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int kx = 16 * (x >> 3) + (x & 7);
-      sc[x] = (kx >= rlo && kx <= rhi) ? sc[x] * a.c : -__builtin_inff();
-      mx = fmaxf(mx, sc[x]);
+      for (int x = 0; x < 16; ++x) {
+        sc[x] *= a.c;
+        mx = fmaxf(mx, sc[x]);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int kx = 16 * (x >> 3) + (x & 7);
+        sc[x] = (kx >= rlo && kx <= rhi) ? sc[x] * a.c : -__builtin_inff();
+        mx = fmaxf(mx, sc[x]);
+      }
     }
     mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
