@@ -476,12 +476,31 @@ fwd_bf16_kernel(const FwdArgs a) {
         // The lane's keys are kx in 0..7 and 16..23.
         vis[j] = rlo <= rhi && ((rlo <= 7 && rhi >= 0) ||
                                 (rlo <= 23 && rhi >= 16));
+      } else if constexpr (CAUSAL) {
+        // Score r holds key kvl + kx with kx = 16 (r / 8) + r % 8 and kvl
+        // this lane's first key of the block: causal hides kx > qrow - kvl
+        // (one compare with a constant per score); keys past NK occur in
+        // the last block only (a uniform branch).
+        const int kvl = kv0 + 8 * h;
+        const int lim = qrow - kvl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kx = 16 * (r >> 3) + (r & 7);
+          if (kx > lim) s[j][r] = -__builtin_inff();
+        }
+        if (kv0 + BC > NK) {
+          const int lim_n = NK - 1 - kvl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kx = 16 * (r >> 3) + (r & 7);
+            if (kx > lim_n) s[j][r] = -__builtin_inff();
+          }
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool ok = key < NK && (!CAUSAL || key <= qrow);
-          if (!ok) s[j][r] = -__builtin_inff();
+          if (key >= NK) s[j][r] = -__builtin_inff();
         }
       }
     }
