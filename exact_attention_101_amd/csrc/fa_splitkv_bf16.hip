@@ -38,7 +38,10 @@ namespace {
 constexpr int D = 128;
 constexpr int NCH = D / 8;            // 16-byte chunks per row
 constexpr int T = 32;                 // keys per tile
-constexpr int NW = 4;                 // waves (independent items) per block
+// Waves (independent items) per block: 5 x 32 KB of double-buffered K / V
+// tiles fill the 160 KB of LDS, so each CU keeps 5 tiles of K and V (80 KB)
+// in flight from HBM (4 waves: 64 KB, 6-14% slower on decode shapes).
+constexpr int NW = 5;
 constexpr int TILE = T * NCH;         // chunks per tile (512)
 constexpr float LN2 = 0.69314718055994531f;
 
@@ -369,9 +372,11 @@ int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk) {
   const long long nrb = (rows + T - 1) / T;
   const long long units = static_cast<long long>(B) * Hkv * nrb;
   const long long nkb = (Nk + T - 1) / T;
-  // About 2048 waves in flight over the 256 CUs (4 waves per CU with this
-  // kernel's LDS use, a couple of rounds), each split at least 4 tiles.
-  long long s = (2048 + units - 1) / units;
+  // About 1024 waves, one round at this kernel's 5 waves per CU, each split
+  // at least 4 tiles.  Measured on decode shapes against 1280, 2048 and 2560
+  // waves: best or tied everywhere (two rounds leave a tail, and split
+  // counts that are not powers of two cut the key range unevenly).
+  long long s = (1024 + units - 1) / units;
   const long long cap = nkb / 4 > 1 ? nkb / 4 : 1;
   if (s > cap) s = cap;
   if (s > SPLITKV_MAX_SPLITS) s = SPLITKV_MAX_SPLITS;
