@@ -160,8 +160,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
 
 /*
  * fa_splitkv_num_splits -- the split count fa_fwd_splitkv is tuned for on
- *   this GPU for the given sizes (about 2048 waves of work, at least 4
- *   32-key tiles per split, at most 256).  Returns 0 for invalid sizes.
+ *   this GPU for the given sizes (about 1024 waves of work, one round at
+ *   five waves per CU; at least 4 32-key tiles per split, at most 256).
+ *   Returns 0 for invalid sizes.
  *   Host-only; enqueues nothing.
  */
 int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk);
