@@ -65,12 +65,25 @@ def _traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
-def _time_launches(fn, steps: int, warmup: int):
+def _time_launches(fn, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """Milliseconds per call of fn() over `steps` back-to-back calls, from
     HIP events on torch's current stream (the stream fn launches on): one
     event before the first call and one after each, so the mean (whole
-    span / steps), median and minimum come from the same timed run."""
+    span / steps), median and minimum come from the same timed run.
+    Warm-up: `warmup` calls, more if needed to fill at least min_warm_ms of
+    back-to-back work (the clock ramps up over the first tens of ms of a
+    burst)."""
     import torch
+    if min_warm_ms > 0:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per = max(e0.elapsed_time(e1) / 3, 1e-3)
+        warmup = max(warmup, int(min_warm_ms / per) + 1)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -207,7 +220,7 @@ def main() -> int:
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
             tm = _time_launches(lambda: fa.forward(qq, kk, vv, causal=ww.causal,
-                                                   out=oo, lse=ll), 20, 20)
+                                                   out=oo, lse=ll), 20, 20, min_warm_ms=30.0)
             m = tm["mean"]
             t = ww.flops / (m * 1e-3) / 1e12
             extras[name] = {"ms": round(m, 4), "ms_median": round(tm["median"], 4),
@@ -227,7 +240,7 @@ def main() -> int:
         fa.forward(q, k, v, causal=w.causal, out=o, lse=lse)
         tm_b = _time_launches(
             lambda: fa.backward(q, k, v, o, lse, dout, causal=w.causal, dq=dq,
-                                dk=dk, dv=dv, workspace=ws), 20, 10)
+                                dk=dk, dv=dv, workspace=ws), 20, 10, min_warm_ms=30.0)
         tb = 2.5 * w.flops / (tm_b["mean"] * 1e-3) / 1e12
         extras["bf16_n8192_backward"] = {
             "ms": round(tm_b["mean"], 4), "ms_median": round(tm_b["median"], 4),
@@ -250,7 +263,7 @@ def main() -> int:
         wd = torch.empty(ns * B_ * H_ * 129, dtype=torch.float32, device=dev)
         tm_d = _time_launches(
             lambda: fa.forward_kv(qd, kd, vd, causal=True, num_splits=ns,
-                                  out=od, lse=ld, workspace=wd), 20, 10)
+                                  out=od, lse=ld, workspace=wd), 20, 10, min_warm_ms=30.0)
         kv_bytes = 2 * kd.numel() * 2
         gbs = kv_bytes / (tm_d["mean"] * 1e-3) / 1e9
         extras["decode_b8_h32_hkv8_nk65536"] = {
@@ -277,7 +290,8 @@ def main() -> int:
         tm_v = _time_launches(
             lambda: fa.forward_varlen(qv_, kv_, vv_, cu, cu, max(lens),
                                       causal=True, window=(win, -1),
-                                      out=ov_, lse=lv_), 20, 10)
+                                      out=ov_, lse=lv_), 20, 10,
+            min_warm_ms=30.0)
         pairs = sum(sum(min(i, win) + 1 for i in range(n)) for n in lens)
         tvl = 4 * 128 * 32 * pairs / (tm_v["mean"] * 1e-3) / 1e12
         extras["varlen_causal_window4096"] = {
@@ -302,7 +316,7 @@ def main() -> int:
                                    .view(np.int32)).to(dev)
             tm_m = _time_launches(
                 lambda: fa.forward_masked(q, k, v, mw_, out=o, lse=lse),
-                20, 10)
+                20, 10, min_warm_ms=30.0)
             vis = float(mbool.sum())
             tmk = 4 * w.d * w.B * w.H * vis / (tm_m["mean"] * 1e-3) / 1e12
             extras[mname] = {
@@ -329,7 +343,7 @@ def main() -> int:
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32,
                              device=dev)
             tm = _time_launches(lambda: fa.forward_fp8(q8, k8, v8, desc,
-                                                       out=oo, lse=ll), 20, 20)
+                                                       out=oo, lse=ll), 20, 20, min_warm_ms=30.0)
             m = tm["mean"]
             t = ww.flops / (m * 1e-3) / 1e12
             key = "fp8_n8192" + ("_hadamard" if rot else "")
@@ -337,7 +351,7 @@ def main() -> int:
                            "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
             _progress(f"{key}: {extras[key]}")
-        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20)["mean"]
+        mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20, min_warm_ms=30.0)["mean"]
         nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
         extras["fp8_quantize_hadamard_per_tensor"] = {
             "ms": round(mq, 4), "GB/s": round(nbytes / (mq * 1e-3) / 1e9, 1),
@@ -352,7 +366,7 @@ def main() -> int:
         a = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
         bt = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
         c = torch.empty((8192, 8192), device=dev, dtype=torch.bfloat16)
-        mg = _time_launches(lambda: torch.matmul(a, bt, out=c), 20, 5)["mean"]
+        mg = _time_launches(lambda: torch.matmul(a, bt, out=c), 20, 5, min_warm_ms=30.0)["mean"]
         tg = 2 * 8192 ** 3 / (mg * 1e-3) / 1e12
         extras["library_gemm_bf16_8192_randn"] = {
             "ms": round(mg, 4), "TFLOP/s": round(tg, 1),
