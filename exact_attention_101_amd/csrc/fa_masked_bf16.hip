@@ -139,43 +139,60 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
     for (int f = 0; f < 8; ++f) sc = mfma(row_frag(kt, li, h, f), qf[f], sc);
     // Lane half h holds keys t T + 16 (x / 8) + 8 h + x % 8.  When every
     // row of the wave sees every key of the tile (dense regions of a mask),
-    // the per-key tests are skipped (a wave-uniform branch).
-    float mx = -__builtin_inff();
+    // the per-key tests are skipped (a wave-uniform branch).  vis: this lane
+    // sees some key of the tile.
+    bool vis = true;
     if (__builtin_amdgcn_ballot_w64(!(qok && mw == 0xFFFFFFFFu)) == 0) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        sc[x] *= a.c;
-        mx = fmaxf(mx, sc[x]);
-      }
+      for (int x = 0; x < 16; ++x) sc[x] *= a.c;
     } else {
       const uint32_t mh = qok ? (mw >> (8 * h)) : 0u;
+      vis = (mh & 0x00FF00FFu) != 0u;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int kx = 16 * (x >> 3) + (x & 7);
         sc[x] = ((mh >> kx) & 1u) ? sc[x] * a.c : -__builtin_inff();
-        mx = fmaxf(mx, sc[x]);
       }
     }
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    // O and l are rescaled only when some row's maximum grew in this tile
-    // (alpha = 1 for every row otherwise); the test is wave-uniform.
-    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
-    }
-    m = m_new;
+    // P is formed against the m already held (any reference gives the same
+    // softmax; a row that has seen no key yet, m = -inf, uses 0).  Only if
+    // a lane's sum of p passes 2^8 (or is not finite), or a row sees its
+    // first key, does the wave take the exact step: the tile's row maximum,
+    // m moved up to it, O and l rescaled, P formed again.  So every p stays
+    // in [0, 2^8] and no maximum is computed on the common path.
     float p[16];
     float sum = 0.f;
+    {
+      const float m_use = (m == -__builtin_inff()) ? 0.f : m;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      p[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
-      sum += p[x];
+      for (int x = 0; x < 16; ++x) {
+        p[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
+        sum += p[x];
+      }
+    }
+    const bool bad = !(sum <= 256.0f) || (m == -__builtin_inff() && vis);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {             // rare
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sc[x]);
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m, mx);
+      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      if (m_new > m) {
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+      }
+      m = m_new;
+      sum = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        p[x] = __builtin_amdgcn_exp2f(sc[x] - m_use);
+        sum += p[x];
+      }
     }
     l += sum;
     bf16x8_t pb[2];
