@@ -317,7 +317,7 @@ fwd_fp8_kernel(const FwdArgs a) {
   // every key of the tile is hidden from the row.
   // A tree of three-input maxima: 32 values -> 12 -> 4 -> 1 in 16
   // v_maximum3_f32 (the maximum is exact, so the order is free).
-  auto tile_max = [&](const f32x16_t (&s)[2]) {
+  auto lane_max = [&](const f32x16_t (&s)[2]) {
     auto at = [&](int j) { return s[j >> 4][j & 15]; };
     float m1[12];
 #pragma unroll
@@ -329,14 +329,21 @@ fwd_fp8_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       m2[i] = maxf(maxf(m1[3 * i], m1[3 * i + 1]), m1[3 * i + 2]);
-    const float mx = maxf(maxf(maxf(m2[0], m2[1]), m2[2]), m2[3]);
-    return half_max(mx);
+    return maxf(maxf(maxf(m2[0], m2[1]), m2[2]), m2[3]);
   };
+  auto tile_max = [&](const f32x16_t (&s)[2]) {
+    return half_max(lane_max(s));
+  };
+  // over(x): how many log2 units a raw score x lies above m0 + P_HEADROOM;
+  // a tile's E must be at least over() of its row maximum.  Monotone in x
+  // (c > 0), so a row's maximum passes E exactly when one of the row's two
+  // lanes' maxima does.
+  auto over = [&](float x) { return fmaf(x, c, -m0) - P_HEADROOM; };
   // E for a tile with row maximum mx (raw score): the smallest integer,
-  // not below the previous one, with mx * c <= m0 + E + P_HEADROOM.
+  // not below the previous one, with over(mx) <= E.
   auto next_e = [&](float mx, int e_prev) {
     if (mx == -__builtin_inff()) return e_prev;
-    const float need = ceilf(mx * c - m0 - P_HEADROOM);
+    const float need = ceilf(over(mx));
     return need > static_cast<float>(e_prev) ? static_cast<int>(need)
                                               : e_prev;
   };
@@ -433,21 +440,28 @@ fwd_fp8_kernel(const FwdArgs a) {
     if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BT);
     s[0] = sn[0];
     s[1] = sn[1];
-    e_cur = next_e(tile_max(s), e_cur);
-    if (__builtin_amdgcn_ballot_w64(e_cur > E_RENORM) != 0) {   // rare
-      // Move the base up by E: O, l and the pending P's scale follow.
-      const int sh = e_cur;
-      const float f = __builtin_ldexpf(1.0f, -sh);
+    // E changes only for a row whose maximum passes over() > E, which one
+    // of the row's two lanes sees alone; the exchange between lane halves
+    // and the update run only when some lane sees it (rare: E never falls).
+    const float lmx = lane_max(s);
+    if (__builtin_amdgcn_ballot_w64(over(lmx) > static_cast<float>(e_cur)) !=
+        0) {
+      e_cur = next_e(half_max(lmx), e_cur);
+      if (__builtin_amdgcn_ballot_w64(e_cur > E_RENORM) != 0) {   // rare
+        // Move the base up by E: O, l and the pending P's scale follow.
+        const int sh = e_cur;
+        const float f = __builtin_ldexpf(1.0f, -sh);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
-      l_run *= f;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
+        l_run *= f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lacc[r] *= f;
-      m0 += static_cast<float>(sh);
-      e_pp = max(e_pp - sh, -127);
-      e_cur = 0;
+        for (int r = 0; r < 16; ++r) lacc[r] *= f;
+        m0 += static_cast<float>(sh);
+        e_pp = max(e_pp - sh, -127);
+        e_cur = 0;
+      }
     }
   };
 
