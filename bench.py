@@ -160,6 +160,117 @@ def _cpu_baseline(w, host, budget_s: float):
     }
 
 
+# Bodies of the issue-rate probes (exact_attention_101_amd/csrc/fa_probe_rates.hip):
+# name -> (id, instructions per round, kind of instruction counted).
+PROBE_BODIES = {
+    "idle": (0, 0, ""),
+    "fma": (1, 16, "v_fma_f32"),
+    "exp": (2, 16, "v_exp_f32"),
+    "exp+fma": (3, 16, "8 v_exp_f32 + 8 v_fma_f32"),
+    "cvt_pk_fp8": (4, 16, "v_cvt_pk_fp8_f32"),
+    "maximum3": (5, 16, "v_maximum3_f32"),
+    "add": (6, 16, "v_add_f32"),
+    "mfma_f8": (7, 4, "v_mfma_scale_f32_32x32x64_f8f6f4"),
+    "mfma_bf16": (8, 4, "v_mfma_f32_32x32x16_bf16"),
+    "mfma_f8+exp": (9, 4, "f8 MFMA, each with 8 exp or 8 fma"),
+    "mfma_bf16+exp": (10, 4, "bf16 MFMA, each with 2 exp + 2 fma"),
+    "exp_chain": (11, 16, "4 x (fma -> exp -> add) + 4 add"),
+}
+
+# (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
+# CU, wave w on SIMD w % 4.
+PROBE_CONFIGS = (
+    [(b, "idle", 4 * n, n) for n in (1, 2, 4)
+     for b in ("fma", "exp", "exp+fma", "add", "cvt_pk_fp8", "maximum3",
+               "exp_chain")]
+    + [(b, "idle", 4 * n, n) for n in (1, 2)
+       for b in ("mfma_f8", "mfma_bf16", "mfma_f8+exp", "mfma_bf16+exp")]
+    + [("mfma_f8", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain")]
+    + [("mfma_bf16", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain")]
+    + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
+)
+
+
+def _rates(iters: int) -> dict:
+    """Cycles per wave64 instruction on one SIMD for each probe body, alone
+    and mixed (see fa_probe_rates.hip)."""
+    import ctypes
+    import statistics
+    import torch
+    import exact_attention_101_amd as fa
+    path = os.path.join(os.path.dirname(fa.__file__), "libfa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built")
+    lib = ctypes.CDLL(path)
+    lib.fa_probe_rates.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2
+    lib.fa_probe_rates.restype = ctypes.c_int
+    torch.cuda.set_device(0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for a, b, waves, na in PROBE_CONFIGS:
+        out = torch.zeros(cus * waves * 3, dtype=torch.int64, device="cuda:0")
+        ia, na_i, _ = PROBE_BODIES[a]
+        ib, nb_i, _ = PROBE_BODIES[b]
+        runs = []
+        for rep in range(4):              # the first run warms the clock
+            rc = lib.fa_probe_rates(ia, ib, waves, na, iters, cus,
+                                    out.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"fa_probe_rates({a}, {b}) = {rc}")
+            torch.cuda.synchronize()
+            if rep:
+                runs.append(out.view(cus, waves, 3).cpu())
+        t = torch.stack(runs)              # [rep, cu, wave, 3]
+        hw = t[0, :, :, 2]
+        simd = ((hw >> 4) & 3).tolist()   # HW_ID bits 5:4
+        is_a = [w < 4 * na for w in range(waves)]
+        # Waves of body A and B on each (workgroup, SIMD); the rates below
+        # come from the SIMDs with the most common composition.
+        comp = {}
+        for g in range(cus):
+            per = {}
+            for w in range(waves):
+                key = per.setdefault(simd[g][w], [0, 0, []])
+                key[0 if is_a[w] else 1] += 1
+                key[2].append(w)
+            for sm, (ka, kb, ws) in per.items():
+                comp.setdefault((ka, kb), []).append((g, ws))
+        (ka, kb), members = max(comp.items(), key=lambda kv: len(kv[1]))
+        cyc = t[:, :, :, 0].double()
+        ref = t[:, :, :, 1].double()
+        ghz = float((cyc / ref).median()) * 0.1
+        row = {"a": a, "b": b, "waves_per_wg": waves,
+               "simd_compositions": {f"A{x}B{y}": len(m) for (x, y), m in
+                                     sorted(comp.items())},
+               "simd_a_waves": ka, "simd_b_waves": kb, "ghz": round(ghz, 3),
+               "hw_id_wg0": [hex(int(x)) for x in hw[0].tolist()]}
+        # A SIMD's throughput for a body is its waves' whole work over the
+        # time its slowest wave of that body took (all waves start together
+        # after a barrier); the fastest wave shows how issue was shared.
+        for name, want_a, n_i, k in ((a, True, na_i, ka),
+                                     (b, False, nb_i, kb)):
+            if k == 0 or n_i == 0:
+                continue
+            slow, fast = [], []
+            for r in range(cyc.shape[0]):
+                for g, ws in members:
+                    d = [float(cyc[r, g, w]) for w in ws if is_a[w] == want_a]
+                    slow.append(max(d))
+                    fast.append(min(d))
+            norm = iters * n_i
+            cs = float(statistics.median(slow)) / norm
+            cf = float(statistics.median(fast)) / norm
+            row[name + "_slowest_wave_cycles_per_instr"] = round(cs, 2)
+            row[name + "_fastest_wave_cycles_per_instr"] = round(cf, 2)
+            row[name + "_simd_cycles_per_instr"] = round(cs / k, 2)
+        rows.append(row)
+        _progress(json.dumps(row))
+    return {"iters": iters, "cus": cus, "bodies": {k: v[2] for k, v in
+                                                   PROBE_BODIES.items()},
+            "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,7 +286,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy "
                          "(reference point for HBM byte counters)")
+    ap.add_argument("--rates", action="store_true",
+                    help="instead of the benchmark: issue-rate probes of one "
+                         "SIMD (cycles per wave64 v_fma_f32, v_exp_f32, "
+                         "MFMA, alone and mixed); prints one JSON line")
+    ap.add_argument("--rates-iters", type=int, default=4096)
     args = ap.parse_args()
+    if args.rates:
+        print(json.dumps(_rates(args.rates_iters)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward kernel runs on a "
               f"single device and this build has no multi-GPU path "

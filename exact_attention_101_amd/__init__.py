@@ -100,6 +100,28 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _out_check(t, name, shape, dtypes, device, align=16):
+    """A caller-supplied output buffer must be exactly what the kernels
+    write: the expected dtype and shape, contiguous, on the inputs' device
+    and aligned as the C ABI requires.  Anything else raises ValueError
+    before any launch (a smaller buffer would be written past its end)."""
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, "
+                         f"got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got "
+                         f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
+    return t
+
+
 def _shape_check(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H(kv), N, d]")
@@ -128,8 +150,10 @@ def forward(q, k, v, *, causal: bool = False, scale=None, out=None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _out_check(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _out_check(lse, "lse", (B, H, N), torch.float32, q.device)
     _check(library().fa_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
@@ -160,15 +184,19 @@ def forward_kv(q, k, v, *, causal: bool = False, scale=None, num_splits=None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _out_check(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _out_check(lse, "lse", (B, H, Nq), torch.float32, q.device)
     need = num_splits * B * H * Nq * (d + 1)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < need or \
-            not workspace.is_contiguous() or workspace.device != q.device:
-        raise ValueError(f"workspace must be a contiguous float32 tensor of "
-                         f"at least {need} elements")
+            not workspace.is_contiguous() or workspace.device != q.device or \
+            workspace.data_ptr() % 16:
+        raise ValueError(f"workspace must be a contiguous, 16-byte aligned "
+                         f"float32 tensor of at least {need} elements on "
+                         f"{q.device}")
     _check(lib.fa_fwd_splitkv(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
@@ -176,14 +204,16 @@ def forward_kv(q, k, v, *, causal: bool = False, scale=None, num_splits=None,
     return out, lse
 
 
-def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *,
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, *,
                    causal: bool = False, window=(-1, -1), scale=None, out=None,
                    lse=None):
     """bf16 forward over a packed batch of sequences of different lengths,
     with an optional sliding window (left, right; -1 = unbounded).
     q: [H, total_q, 128]; k, v: [Hkv, total_k, 128]; cu_seqlens_q/k: int32
-    CUDA tensors of B + 1 row offsets.  Returns (o bf16 [H, total_q, 128],
-    lse fp32 [H, total_q])."""
+    CUDA tensors of B + 1 row offsets.  max_seqlen_q: the longest query
+    sequence; None reads it from cu_seqlens_q (one device-to-host copy).  A
+    value below the longest sequence leaves that sequence's rows past it
+    unwritten.  Returns (o bf16 [H, total_q, 128], lse fp32 [H, total_q])."""
     import torch
     for t in (q, k, v):
         if t.dim() != 3 or not t.is_contiguous() or not t.is_cuda or \
@@ -202,12 +232,17 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *,
     Hkv, total_k, dk = k.shape
     if k.shape != v.shape or dk != d:
         raise ValueError("k/v shape does not match q")
+    if max_seqlen_q is None:
+        max_seqlen_q = max(int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max()),
+                           1)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _out_check(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _out_check(lse, "lse", (H, total_q), torch.float32, q.device, align=4)
     wl, wr = window
     _check(library().fa_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -249,8 +284,10 @@ def forward_masked(q, k, v, mask, *, scale=None, out=None, lse=None):
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _out_check(out, "out", q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _out_check(lse, "lse", (B, H, Nq), torch.float32, q.device, align=4)
     _check(library().fa_fwd_masked(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), mask.data_ptr(), bstride, hstride, B, H, Hkv, Nq, Nk,
@@ -283,13 +320,16 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale=None,
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _out_check(t, name, ref.shape, torch.bfloat16, q.device)
     if workspace is None:
         workspace = torch.empty(2 * B * H * N, dtype=torch.float32,
                                 device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * N \
-            or not workspace.is_contiguous() or workspace.device != q.device:
-        raise ValueError("workspace must be a contiguous float32 tensor of "
-                         "at least 2 * B * H * N elements")
+            or not workspace.is_contiguous() or workspace.device != q.device \
+            or workspace.data_ptr() % 16:
+        raise ValueError("workspace must be a contiguous, 16-byte aligned "
+                         "float32 tensor of at least 2 * B * H * N elements")
     _check(library().fa_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -313,12 +353,16 @@ def forward_fp8(q8, k8, v8, descale_qkv=None, *, causal: bool = False,
                 not descale_qkv.is_cuda or not descale_qkv.is_contiguous():
             raise ValueError("descale_qkv must be a contiguous float32 CUDA "
                              "tensor of 3 elements")
+        if descale_qkv.device != q8.device:
+            raise ValueError(f"descale_qkv must be on {q8.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    _out_check(out, "out", (B, H, N, d), torch.bfloat16, q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _out_check(lse, "lse", (B, H, N), torch.float32, q8.device)
     _check(library().fa_fwd_fp8(
         q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
@@ -339,8 +383,12 @@ def quantize_fp8(x, signs=None, *, out=None, amax_descale=None):
     rows = x.numel() // d if d else 0
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _out_check(out, "out", x.shape, (torch.uint8, torch.float8_e4m3fn),
+               x.device)
     if amax_descale is None:
         amax_descale = torch.empty(2, dtype=torch.float32, device=x.device)
+    _out_check(amax_descale, "amax_descale", (2,), torch.float32, x.device,
+               align=4)
     sign_buf = None
     if signs is not None:
         import numpy as np

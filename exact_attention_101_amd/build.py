@@ -12,6 +12,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
+# Issue-rate probes of the SIMD (measurement support, its own library).
+PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
+PROBE_SOURCES = ["fa_probe_rates.hip"]
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_quant.hip",
            "fa_bwd_bf16.hip", "fa_splitkv_bf16.hip", "fa_varlen_bf16.hip",
            "fa_masked_bf16.hip"]
@@ -42,11 +45,10 @@ FLAGS_DEVICE_ASM = [*CODEGEN, "--cuda-device-only", "-S",
                     "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libfa.so (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+def _compile(out: str, sources, extra=(), verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,7 +60,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libfa.so, and the probe library
+    (always rebuilds)."""
+    _compile(LIB, SOURCES, verbose=verbose)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose=verbose)
     return LIB
 
 

@@ -207,14 +207,24 @@ FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v,
   if (H % Hkv != 0 || !isfinite(scale) || window_left < -1 ||
       window_right < -1)
     return FA_ERR_INVALID_ARGUMENT;
-  if (static_cast<long long>(H) * total_q > (1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(H) * total_q > (1LL << 40) ||
+      total_q > fa::VARLEN_MAX_ROWS || total_k > fa::VARLEN_MAX_ROWS)
+    return FA_ERR_INVALID_ARGUMENT;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
     return FA_ERR_MISALIGNED;
-  const int right = causal ? 0 : window_right;
+  // A window at least as wide as every sequence is the unbounded one: with
+  // query i of a sequence of NQ queries and NK keys seeing key j iff
+  // i + off - left <= j <= i + off + right (off = NK - NQ, 0 <= j < NK),
+  // left >= NK - 1 or right >= NQ - 1 hides nothing, and NK <= total_k,
+  // NQ <= total_q.  Clamping keeps the kernels' i + off +- window sums
+  // within int range for any window the caller passes.
+  if (window_left >= total_k) window_left = -1;
+  int right = causal ? 0 : window_right;
+  if (right >= total_q) right = -1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // Windows bounded on both sides and narrower than VARLEN_NARROW keys go
   // to the 128-row kernel, whose waves skip the tiles outside their own

@@ -124,6 +124,9 @@ constexpr int MASK_MAX_NK = 262144;   // keys a mask may cover
 // Variable-length windows with left + right below this many keys (both
 // bounded) run on the 128-row kernel, wider ones on the pipelined kernel.
 constexpr int VARLEN_NARROW = 512;
+// Packed rows per head a variable-length batch may hold (queries or keys):
+// row, offset and window sums then stay below 2^31.
+constexpr int VARLEN_MAX_ROWS = 1 << 29;
 
 // x if ok, else zero; selected per 32-bit component (a select of the whole
 // vector can end up in private memory).

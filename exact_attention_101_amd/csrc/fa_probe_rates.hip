@@ -1,0 +1,273 @@
+// Issue-rate probes for gfx950 (MI355X): how many cycles of a SIMD one
+// wave64 instruction of each kind the softmax and the matrix products use
+// occupies, alone and mixed, at 1 to 4 waves per SIMD.  Built into its own
+// library (libfa_probe.so), not into libfa.so: it is measurement support for
+// the attention kernels' roofline, not part of the attention path.
+//
+// The question it answers is the one the FlashAttention-4 article
+// («Оптимизируйте производительность с FlashAttention-4», paragraph 3)
+// raises for Blackwell: whether the exponential unit, rather than the matrix
+// cores, bounds the forward, and whether computing some exponentials with
+// ordinary FMA instructions would pay.  On this chip that depends on the
+// cost of v_exp_f32 against v_fma_f32 on the same SIMD and on whether the
+// two overlap, which the probes measure.
+//
+// Each wave runs `iters` rounds of one block of independent instructions
+// (16 VALU instructions over 16 independent chains, or 4 MFMAs into 4
+// accumulators) written as inline assembly or builtins the compiler cannot
+// fold, between two reads of the shader clock (s_memtime) and of the
+// 100 MHz reference clock (s_memrealtime).  The waves of one workgroup run
+// one of two bodies each (the first 4 * na waves body A, the rest body B;
+// wave w sits on SIMD w % 4), one workgroup per CU (it reserves 96 KiB of
+// LDS).  Nothing is written but the per-wave timings.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fa_probe.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+
+enum Body {
+  B_IDLE = 0,     // no work
+  B_FMA = 1,      // 16 x v_fma_f32
+  B_EXP = 2,      // 16 x v_exp_f32
+  B_EXP_FMA = 3,  // 8 x v_exp_f32 interleaved with 8 x v_fma_f32
+  B_CVT8 = 4,     // 16 x v_cvt_pk_fp8_f32
+  B_MAX3 = 5,     // 16 x v_maximum3_f32
+  B_ADD = 6,      // 16 x v_add_f32
+  B_MFMA8 = 7,    // 4 x v_mfma_scale_f32_32x32x64_f8f6f4
+  B_MFMA16 = 8,   // 4 x v_mfma_f32_32x32x16_bf16
+  B_MFMA8_EXP = 9,    // 1 f8 MFMA + 8 exp + 8 fma (one softmax slot)
+  B_MFMA16_EXP = 10,  // 1 bf16 MFMA + 4 exp + 4 fma
+  B_EXP_CHAIN = 11,   // 4 x (v_fma_f32 -> v_exp_f32 -> v_add_f32), + 4 adds
+};
+
+struct Regs {
+  float x[16];
+  float y, z;
+  int w[8];
+  f32x16_t acc[4];
+};
+
+__device__ __forceinline__ void fma16(Regs& r, int first, int n) {
+#pragma unroll
+  for (int i = first; i < first + n; ++i)
+    asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(r.x[i]) : "v"(r.y), "v"(r.z));
+}
+
+__device__ __forceinline__ void exp16(Regs& r, int first, int n) {
+#pragma unroll
+  for (int i = first; i < first + n; ++i)
+    asm volatile("v_exp_f32 %0, %0" : "+v"(r.x[i]));
+}
+
+template <int BODY>
+__device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
+                                         const bf16x8_t& a16) {
+  if constexpr (BODY == B_FMA) {
+    fma16(r, 0, 16);
+  } else if constexpr (BODY == B_EXP) {
+    exp16(r, 0, 16);
+  } else if constexpr (BODY == B_EXP_FMA) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      asm volatile("v_exp_f32 %0, %0" : "+v"(r.x[i]));
+      asm volatile("v_fma_f32 %0, %0, %1, %2"
+                   : "+v"(r.x[8 + i]) : "v"(r.y), "v"(r.z));
+    }
+  } else if constexpr (BODY == B_CVT8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2"
+                   : "+v"(r.w[i]) : "v"(r.x[2 * i]), "v"(r.x[2 * i + 1]));
+      asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2 op_sel:[0,0,1]"
+                   : "+v"(r.w[i]) : "v"(r.x[2 * i + 1]), "v"(r.x[2 * i]));
+    }
+  } else if constexpr (BODY == B_MAX3) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      asm volatile("v_maximum3_f32 %0, %0, %1, %2"
+                   : "+v"(r.x[i]) : "v"(r.y), "v"(r.z));
+  } else if constexpr (BODY == B_ADD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      asm volatile("v_add_f32 %0, %0, %1" : "+v"(r.x[i]) : "v"(r.y));
+  } else if constexpr (BODY == B_MFMA8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a8, a8, r.acc[j], 0, 0, 0, 127, 0, 127);
+      asm volatile("" : "+v"(r.acc[j]));
+    }
+  } else if constexpr (BODY == B_MFMA16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a16, a16, r.acc[j],
+                                                         0, 0, 0);
+      asm volatile("" : "+v"(r.acc[j]));
+    }
+  } else if constexpr (BODY == B_MFMA8_EXP) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a8, a8, r.acc[j], 0, 0, 0, 127, 0, 127);
+      asm volatile("" : "+v"(r.acc[j]));
+      if (j % 2 == 0) {
+        exp16(r, 0, 8);
+      } else {
+        fma16(r, 8, 8);
+      }
+    }
+  } else if constexpr (BODY == B_MFMA16_EXP) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a16, a16, r.acc[j],
+                                                         0, 0, 0);
+      asm volatile("" : "+v"(r.acc[j]));
+      exp16(r, 4 * j, 2);
+      fma16(r, 4 * j + 2, 2);
+    }
+  } else if constexpr (BODY == B_EXP_CHAIN) {
+    // The softmax's dependent sequence: scale and shift, exponential, sum.
+    // Written with builtins so that the compiler inserts the wait states a
+    // use of a transcendental result needs.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = __builtin_amdgcn_exp2f(fmaf(r.x[i], r.y, r.z));
+      r.x[8 + i] += t;
+      asm volatile("" : "+v"(r.x[8 + i]));
+      r.x[i] += 1.0f;
+      asm volatile("" : "+v"(r.x[i]));
+    }
+  }
+}
+
+template <int BODY>
+__device__ __forceinline__ void run(Regs& r, int iters, const i32x8_t& a8,
+                                    const bf16x8_t& a16) {
+  for (int it = 0; it < iters; ++it) round_of<BODY>(r, a8, a16);
+}
+
+template <int A, int B>
+__global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
+                                                     int iters, int na,
+                                                     float seed) {
+  __shared__ float reserve[24576];      // 96 KiB: one workgroup per CU
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  Regs r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r.x[i] = seed * (i + 1) + 1e-3f * lane;
+  r.y = 0.999f;
+  r.z = seed;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.w[i] = i;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
+  const int s8 = 0x38383838 + (lane & 1);   // e4m3 codes near 1.0
+  const i32x8_t a8 = {s8, s8, s8, s8, s8, s8, s8, s8};
+  bf16x8_t a16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a16[i] = static_cast<__bf16>(seed + 0.5f * i);
+
+  __syncthreads();
+  const uint64_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  if ((wave >> 2) < na)
+    run<A>(r, iters, a8, a16);
+  else
+    run<B>(r, iters, a8, a16);
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+
+  // Keep every result alive (never true for the seeds used).
+  float sink = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sink += r.x[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.w[i]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sink += r.acc[j][lane & 15];
+  if (iters < 0) {
+    reserve[tid] = sink;
+    __syncthreads();
+    out[0] = static_cast<unsigned long long>(reserve[(tid + 1) & 1023]);
+  }
+  if (lane == 0) {
+    const size_t g = (static_cast<size_t>(blockIdx.x) * (blockDim.x >> 6) +
+                      wave) * 3;
+    out[g + 0] = t1 - t0;
+    out[g + 1] = r1 - r0;
+    out[g + 2] = hw;
+  }
+}
+
+template <int A, int B>
+hipError_t launch(unsigned long long* out, int iters, int na, int waves,
+                  int grid, hipStream_t s) {
+  hipLaunchKernelGGL((probe_kernel<A, B>), dim3(grid), dim3(64 * waves), 0, s,
+                     out, iters, na, 1.0e-3f);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*launch_fn)(unsigned long long*, int, int, int, int,
+                                hipStream_t);
+
+template <int A>
+launch_fn pick_b(int b) {
+  switch (b) {
+    case B_IDLE: return launch<A, B_IDLE>;
+    case B_FMA: return launch<A, B_FMA>;
+    case B_EXP: return launch<A, B_EXP>;
+    case B_EXP_FMA: return launch<A, B_EXP_FMA>;
+    case B_CVT8: return launch<A, B_CVT8>;
+    case B_MAX3: return launch<A, B_MAX3>;
+    case B_ADD: return launch<A, B_ADD>;
+    case B_MFMA8: return launch<A, B_MFMA8>;
+    case B_MFMA16: return launch<A, B_MFMA16>;
+    case B_MFMA8_EXP: return launch<A, B_MFMA8_EXP>;
+    case B_MFMA16_EXP: return launch<A, B_MFMA16_EXP>;
+    case B_EXP_CHAIN: return launch<A, B_EXP_CHAIN>;
+    default: return nullptr;
+  }
+}
+
+launch_fn pick(int a, int b) {
+  switch (a) {
+    case B_FMA: return pick_b<B_FMA>(b);
+    case B_EXP: return pick_b<B_EXP>(b);
+    case B_EXP_FMA: return pick_b<B_EXP_FMA>(b);
+    case B_CVT8: return pick_b<B_CVT8>(b);
+    case B_MAX3: return pick_b<B_MAX3>(b);
+    case B_ADD: return pick_b<B_ADD>(b);
+    case B_MFMA8: return pick_b<B_MFMA8>(b);
+    case B_MFMA16: return pick_b<B_MFMA16>(b);
+    case B_MFMA8_EXP: return pick_b<B_MFMA8_EXP>(b);
+    case B_MFMA16_EXP: return pick_b<B_MFMA16_EXP>(b);
+    case B_EXP_CHAIN: return pick_b<B_EXP_CHAIN>(b);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+// Contract in include/fa_probe.h.
+extern "C" __attribute__((visibility("default"))) int fa_probe_rates(
+    int a, int b, int waves, int na, int iters, int grid,
+    unsigned long long* out, void* stream) {
+  if (!out || waves < 4 || waves > 16 || waves % 4 != 0 || na < 0 ||
+      na > waves / 4 || iters < 1 || grid < 1)
+    return 1;
+  const launch_fn f = pick(a, b);
+  if (!f) return 1;
+  return f(out, iters, na, waves, grid, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? 0
+             : 4;
+}

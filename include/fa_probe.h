@@ -1,0 +1,48 @@
+/*
+ * fa_probe.h -- C ABI of libfa_probe.so: issue-rate probes of one SIMD of
+ * the MI355X (gfx950).  Measurement support for the attention kernels'
+ * roofline, not part of the attention path.
+ *
+ * The FlashAttention-4 article («Оптимизируйте производительность с
+ * FlashAttention-4», paragraph 3) attributes the forward's cost on Blackwell
+ * to the exponential unit rather than the tensor cores, and computes part of
+ * the exponentials with ordinary FMA instructions.  Whether either holds on
+ * this chip depends on what a v_exp_f32 costs a SIMD next to a v_fma_f32,
+ * the packing and maximum instructions of the softmax, and the matrix
+ * instructions, and on how they overlap; these probes measure exactly that.
+ */
+#ifndef FA_PROBE_H_
+#define FA_PROBE_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_probe_rates -- one timing launch.
+ *   a, b    instruction bodies (ids as in fa_probe_rates.hip: 1 v_fma_f32,
+ *           2 v_exp_f32, 3 exp + fma interleaved, 4 v_cvt_pk_fp8_f32,
+ *           5 v_maximum3_f32, 6 v_add_f32, 7 f8 MFMA 32x32x64, 8 bf16 MFMA
+ *           32x32x16, 9 f8 MFMA with exp / fma, 10 bf16 MFMA with exp and
+ *           fma, 11 fma -> exp -> add chains; b may also be 0, idle).
+ *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
+ *           CU, so waves / 4 waves on each SIMD).
+ *   na      the first 4 * na waves run body a, the others body b.
+ *   iters   rounds of the body per wave, >= 1.
+ *   grid    workgroups (the CU count for one per CU).
+ *   out     device, caller-owned, grid * waves * 3 uint64 (written): per
+ *           wave in (workgroup, wave) order, shader-clock cycles between the
+ *           two clock reads, 100 MHz reference ticks over the same span, and
+ *           the wave's HW_ID register (SIMD in bits 5:4).
+ *   stream  hipStream_t or NULL; one kernel is enqueued.
+ *   Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the
+ *   launch failed.
+ */
+int fa_probe_rates(int a, int b, int waves, int na, int iters, int grid,
+                   unsigned long long* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_PROBE_H_ */

@@ -42,6 +42,27 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_header():
+    """libfa_probe.so (issue-rate probes, measurement support) exports what
+    include/fa_probe.h declares, and rejects bad arguments without a GPU."""
+    from exact_attention_101_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    text = open(os.path.join(ROOT, "include", "fa_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["fa_probe_rates"]
+    plib = ctypes.CDLL(build.PROBE_LIB)
+    f = plib.fa_probe_rates
+    f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2
+    f.restype = ctypes.c_int
+    assert f(1, 0, 4, 1, 8, 1, None, None) == 1          # null output
+    assert f(1, 0, 6, 1, 8, 1, A, None) == 1             # waves not 4k
+    assert f(1, 0, 4, 2, 8, 1, A, None) == 1             # na > waves / 4
+    assert f(99, 0, 4, 1, 8, 1, A, None) == 1            # unknown body
+    assert f(0, 0, 4, 1, 8, 1, A, None) == 1             # body a idle
+
+
 def test_version_and_status_strings(lib):
     assert lib.fa_version() == 100
     for s in range(0, 6):
