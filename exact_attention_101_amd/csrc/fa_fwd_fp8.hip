@@ -9,40 +9,39 @@
 //   * Inputs are e4m3 codes with per-tensor descales dQ, dK, dV read from
 //     device memory (no host synchronisation).  The score scale folds in
 //     dQ * dK; dV multiplies the output in the epilogue.
-//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4
-//     with neutral (2^0) block scales, fp32 accumulation.  Each lane owns
-//     one query; the lane's 32 scores of a 64-key tile, rounded to e4m3, are
-//     exactly its 32-byte B operand of the P V product (K rows in sigma
-//     order, fa_common.h), and the V^T operand comes from the transposing
-//     ds_read_b64_tr_b8.
-//   * Workgroup = 4 waves of 32 query rows (BR = 128), two workgroups per
-//     CU, so two waves per SIMD: with fp8 the matrix work per score halves,
-//     so the vector work of the softmax needs the issue slots of two waves,
-//     and waves of different workgroups never wait at each other's barrier.
-//     K and V tiles of 64 keys go from HBM/L2 straight into LDS with
-//     buffer_load_dwordx4 ... lds (two 1 KB windows of each per wave),
-//     double-buffered.
-//   * A three-stage software pipeline runs in every step t: one issue slot
-//     per MFMA pair, the scores MFMA of tile t+1, p = exp2(S c - m + 8) for
-//     four score pairs of tile t, the P V MFMA of tile t-1, then the e4m3
-//     packs and lane sums of those pairs (the intra-group overlap of the
-//     FlashAttention-3 summary, section «Assincronia»).
+//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4,
+//     fp32 accumulation.  Each lane owns one query; the lane's 32 scores of
+//     a 64-key tile, rounded to e4m3, are exactly its 32-byte B operand of
+//     the P V product (K rows in sigma order, fa_common.h), and the V^T
+//     operand comes from the transposing ds_read_b64_tr_b8.
 //   * P is stored as p * 2^8 in e4m3 (keeps small weights out of the
 //     subnormal range), which must stay at most 448.  O and l are kept
-//     relative to a per-row base m0 (block 0's row maximum) and are never
+//     relative to a per-row base m0 (tile 0's row maximum) and are never
 //     rescaled: tile t forms p against m0 + E_t, where E_t is the smallest
 //     integer (never decreasing) that keeps the tile's row maximum within
 //     log2(448/256) of it, and the P V MFMA takes the per-lane block scale
 //     2^E_t of the f8f6f4 instruction, so O accumulates p * 2^8 * 2^E_t
 //     relative to m0 exactly.  Two row sums follow it: lq over the e4m3
-//     values the product used, from one more MFMA per tile with an all-ones
-//     A operand and the same block scale (O = acc / lq, so a row whose
-//     weight sits on one key is not off by that key's rounding, up to 2^-4),
-//     and l, the lanes' fp32 sums of p before rounding times 2^E_t (the
-//     LSE).  Both carry the same 2^8, which cancels in O and is removed from
-//     the LSE.  Only if E passes 64 (scores rising more than 64
-//     log2 units above block 0) are O and l renormalised, to keep fp32
-//     headroom.
+//     values the product used (O = acc / lq, so a row whose weight sits on
+//     one key is not off by that key's rounding, up to 2^-4), and l, the
+//     lanes' fp32 sums of p before rounding times 2^E_t (the LSE).  Both
+//     carry the same 2^8, which cancels in O and is removed from the LSE.
+//     Only if E passes 64 (scores rising more than 64 log2 units above
+//     tile 0) are O and the sums renormalised, to keep fp32 headroom.
+//
+// The vector work of the softmax per 64-key tile and 32 query rows (32
+// exponentials, 16 e4m3 packs, 32 scale FMAs, 32 sums and the 16-instruction
+// tile maximum) takes more issue time than the tile's nine matrix
+// instructions: one wave issues a v_exp_f32 only every ~16 cycles, against
+// ~8.6 for the SIMD as a whole, and exponentials and FMAs share issue (the
+// issue-rate probes, fa_probe_rates.hip).  So a wave does its tiles in
+// order (scores, tile maximum and E, exponentials and packs, P V) and three
+// waves per SIMD hide each other's latencies; a software pipeline inside one
+// wave (scores of tile t+1 and P V of tile t-1 around the softmax of tile t)
+// needs ~250 registers and so allows only two waves, and measured 6-7%
+// slower.  With at most 168 registers per wave: no second score buffer, P
+// formed and consumed in the same tile, operand fragments read one product
+// ahead, and the row sums of the rounded P from one 16x16x128 MFMA.
 #include "fa_common.h"
 
 namespace fa {
@@ -50,10 +49,7 @@ namespace fa {
 namespace {
 
 constexpr int D = 128;
-constexpr int BT = 64;               // keys per tile (= per step)
-// Waves per workgroup.  Two workgroups share a CU (registers and LDS allow
-// it), so each SIMD runs two waves that never wait on each other's barrier.
-constexpr int NWAVE_FP8 = 4;
+constexpr int BT = 64;               // keys per tile
 constexpr int NCH = D / 16;          // 16-byte chunks per row (8)
 constexpr float P_SHIFT = 8.0f;      // P is stored as p * 2^8
 // p * 2^8 <= 448 (largest finite e4m3) when the score is at most
@@ -62,11 +58,6 @@ constexpr float P_HEADROOM = 0.8f;
 constexpr int E_RENORM = 64;         // renormalise O, l beyond this shift
 
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
-
-template <bool V>
-struct Tag {
-  static constexpr bool value = V;
-};
 
 // K tile [key][d] bytes: physical 16-byte chunk of (row r, chunk c).  The
 // reading lane i uses row r = sigma(i) (+32 kb), so the XOR term depends on
@@ -145,23 +136,40 @@ __device__ __forceinline__ f32x16_t mfma_f8_bscale(const i32x8_t& a,
 // LDS at `dst` + 16 * lane.  Offsets past the descriptor's size read zeros.
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
                                             const uint4* dst,
-                                            uint32_t voffset) {
+                                            uint32_t voffset,
+                                            uint32_t soffset = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset, 0, 0,
-      0);
+      rsrc, (__attribute__((address_space(3))) void*)(dst), 16, voffset,
+      soffset, 0, 0);
 }
 
-template <bool CAUSAL, int NWAVE>
-__global__ void __launch_bounds__(64 * NWAVE, 1)
+// The kernel (three waves per SIMD, design above):
+//   * Workgroup: 4 waves x 32 rows (BR = 128), three workgroups per CU
+//     (32 KB of LDS each).  K and V tiles of 64 keys are copied into LDS by
+//     DMA one tile ahead (double-buffered): at the start of tile t every
+//     wave waits for its copies of tile t, meets the others at the barrier
+//     (so stage (t+1) % 2, tile t-1's, is free) and starts those of t+1.
+//   * Row sum of the rounded P from v_mfma_scale_f32_16x16x128_f8f6f4 with
+//     B = the lane's 32 packed P bytes.  In that product lane l supplies
+//     column l % 16 of B (and row l % 16 of A) with k in [16 j, 16 j + 16)
+//     (registers 0-3) and [64 + 16 j, 64 + 16 j + 16) (registers 4-7),
+//     j = l / 16 (measured with one-hot operands); lane l of P holds query
+//     l % 32, key half l / 32.  A = ones in lanes 0 and 32 (row 0) and 17
+//     and 49 (row 1) gives C[0][n] = lq(query n) and C[1][n] = lq(query
+//     n + 16), both in lane n < 16.  The E8M0 scale of k block b of column n
+//     is taken from lane n + 16 b, which mixes queries n and n + 16, so this
+//     product runs with neutral scales: it sums the rounded P as formed
+//     (relative to m0 + E) while E stays put, and whenever some row's E
+//     moves the sums are folded into fp32 totals times 2^E first.
+template <bool CAUSAL>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const FwdArgs a) {
-  constexpr int BR = 32 * NWAVE;               // query rows per workgroup
-  // 1 KB copy windows per tile and operand, and how many each wave issues.
+  constexpr int NWAVE = 4;
+  constexpr int BR = 32 * NWAVE;
   constexpr int NWIN = BT * NCH / (64 * NWAVE);
-  static_assert(NWIN * 64 * NWAVE == BT * NCH, "whole windows per wave");
-  // Window w of wave v covers rows 8 (v + NWAVE w) .. +7: a multiple of 32
-  // rows apart, so the swizzles (which depend on the row mod 32) repeat.
-  static_assert(NWIN == 1 || (8 * NWAVE) % 32 == 0, "window spacing");
-  constexpr uint32_t WIN_BYTES = 8 * NWAVE * D;  // global offset per window
+  static_assert(NWIN == 2, "two copy windows per tile and operand");
+  constexpr uint32_t WIN_BYTES = 8 * NWAVE * D;
   __shared__ uint4 Ks0[BT * NCH];
   __shared__ uint4 Ks1[BT * NCH];
   __shared__ uint4 Vs0[BT * NCH];
@@ -169,7 +177,7 @@ fwd_fp8_kernel(const FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int h = lane >> 5;
 
@@ -190,9 +198,6 @@ fwd_fp8_kernel(const FwdArgs a) {
     dk = a.descale[1];
     dv = a.descale[2];
   }
-  // Scores enter exp2 as S * c with c = |scale| dQ dK log2(e); a negative
-  // product is handled by negating Q's codes (sign bit) on load.  c is
-  // floored so that a masked score (-inf) always gives p = 0.
   const float cs = a.scale * dq * dk * 1.4426950408889634f;
   const bool neg = cs < 0.f;
   const float c = fmaxf(fabsf(cs), 1e-30f);
@@ -204,7 +209,6 @@ fwd_fp8_kernel(const FwdArgs a) {
   const uint8_t* vp = static_cast<const uint8_t*>(a.v) +
                       (static_cast<int64_t>(b) * a.Hkv + hk) * N * D;
 
-  // Q -> registers: k-step s covers d in [64 h + 32 s, +32) for lane half h.
   i32x8_t qf[2];
   {
     const uint32_t flip = neg ? 0x80808080u : 0u;
@@ -222,9 +226,6 @@ fwd_fp8_kernel(const FwdArgs a) {
     }
   }
 
-  // ---- tile copies: wave w fills 64-slot window w of each stage ----
-  // Lane L writes physical slot 64 w + L = row * NCH + physical chunk; the
-  // logical chunk is recovered with the (involutive) swizzle.
   uint32_t koff, voff;
   {
     const int slot = 64 * wave + lane;
@@ -233,13 +234,8 @@ fwd_fp8_kernel(const FwdArgs a) {
     voff = static_cast<uint32_t>(r * D + 16 * vswz(r, p));
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;   // last key needed + 1
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BT - 1) / BT;
-  // Steps 1 .. nsteps run in pairs; step t ends with O += P(t-1) V(t-1), so
-  // the last real tile is done at step ntiles.  Tiles past the real ones
-  // are virtual: their copies read zeros (the descriptors end at kv_end) and
-  // their scores are masked, so their p are 0.
-  const int nsteps = (ntiles + 1) & ~1;
 
   auto rsrc_at = [&](const uint8_t* base, int kv0) {
     const int rows = max(kv_end - kv0, 0);
@@ -247,10 +243,16 @@ fwd_fp8_kernel(const FwdArgs a) {
         const_cast<uint8_t*>(base + static_cast<int64_t>(kv0) * D), 0,
         rows * D, 0x00020000);
   };
+  auto copy_tile = [&](int t, const uint4* ks, const uint4* vs) {
+    const auto rk = rsrc_at(kp, t * BT);
+    const auto rv = rsrc_at(vp, t * BT);
+#pragma unroll
+    for (int w = 0; w < NWIN; ++w) {
+      copy_to_lds(rk, ks + 64 * (wave + NWAVE * w), koff, w * WIN_BYTES);
+      copy_to_lds(rv, vs + 64 * (wave + NWAVE * w), voff, w * WIN_BYTES);
+    }
+  };
 
-  // ---- LDS read offsets ----
-  //   K fragment (kb, s): row 32 kb + sigma(li), logical chunks 4 h + 2 s
-  //   and 4 h + 2 s + 1.
   auto kfrag = [&](const uint4* ks, int kb, int s) {
     const int r = 32 * kb + sigma(li);
     const uint4* row = ks + r * NCH;
@@ -259,14 +261,10 @@ fwd_fp8_kernel(const FwdArgs a) {
     return i32x8_t{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
                    (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
   };
-  //   Transposed V fragment of d block db: group g = lane / 16, lanes 2R + j
-  //   of the group read key row 16 t8 + 8 h + R at bytes [32 db + 16 (g % 2)
-  //   + 8 j, +8); output lane i then holds 8 keys of d = 32 db + 16 (g % 2)
-  //   + i, for t8 = 0..3 (bytes 8 t8 .. 8 t8 + 7 of the A operand).
   const int tr_g = lane >> 4;
   const int tr_R = (lane >> 1) & 7;
   const int tr_j = lane & 1;
-  const int tr_c = 2 * (tr_g & 1) + tr_j;        // 8-byte unit in a 32-d block
+  const int tr_c = 2 * (tr_g & 1) + tr_j;
   auto vfrag = [&](const uint4* vs, int db) {
     int av[8];
 #pragma unroll
@@ -286,17 +284,14 @@ fwd_fp8_kernel(const FwdArgs a) {
   f32x16_t oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m0 = 0.f;                       // per-row base, log2 units
-  int e_cur = 0;                        // E of the tile whose P is formed
-  float l_run = 0.f;                    // this lane's half of sum p*2^8*2^E
-  // Row sums of the e4m3 P the product used, times 2^E, from a fifth MFMA
-  // with an all-ones A: every row of the result is the column sum, so each
-  // lane's element 0 is the sum for its own query.
-  f32x16_t lacc = f32x16_t{};
-  const int ONE4 = 0x38383838;          // four e4m3 1.0
-  const i32x8_t ones = {ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4};
+  // Row sums of the rounded P since E last moved (lane n < 16: queries n,
+  // n + 16), and their totals times 2^E.
+  float lraw0 = 0.f, lraw1 = 0.f;
+  float lq0 = 0.f, lq1 = 0.f;
+  float m0 = 0.f;
+  int e_cur = 0;
+  float l_run = 0.f;
 
-  // Lane half h holds keys kv0 + 32 kb + 16 (r / 8) + 8 h + (r % 8).
   auto apply_mask = [&](f32x16_t (&s)[2], int kv0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -312,11 +307,6 @@ fwd_fp8_kernel(const FwdArgs a) {
     const int kv0 = t * BT;
     return (kv0 + BT > N) || (CAUSAL && kv0 + BT - 1 > qw0);
   };
-
-  // Row maximum of a tile's (masked) scores, both lane halves; -inf if
-  // every key of the tile is hidden from the row.
-  // A tree of three-input maxima: 32 values -> 12 -> 4 -> 1 in 16
-  // v_maximum3_f32 (the maximum is exact, so the order is free).
   auto lane_max = [&](const f32x16_t (&s)[2]) {
     auto at = [&](int j) { return s[j >> 4][j & 15]; };
     float m1[12];
@@ -331,179 +321,180 @@ fwd_fp8_kernel(const FwdArgs a) {
       m2[i] = maxf(maxf(m1[3 * i], m1[3 * i + 1]), m1[3 * i + 2]);
     return maxf(maxf(maxf(m2[0], m2[1]), m2[2]), m2[3]);
   };
-  auto tile_max = [&](const f32x16_t (&s)[2]) {
-    return half_max(lane_max(s));
-  };
-  // over(x): how many log2 units a raw score x lies above m0 + P_HEADROOM;
-  // a tile's E must be at least over() of its row maximum.  Monotone in x
-  // (c > 0), so a row's maximum passes E exactly when one of the row's two
-  // lanes' maxima does.
   auto over = [&](float x) { return fmaf(x, c, -m0) - P_HEADROOM; };
-  // E for a tile with row maximum mx (raw score): the smallest integer,
-  // not below the previous one, with over(mx) <= E.
   auto next_e = [&](float mx, int e_prev) {
     if (mx == -__builtin_inff()) return e_prev;
     const float need = ceilf(over(mx));
     return need > static_cast<float>(e_prev) ? static_cast<int>(need)
                                               : e_prev;
   };
-
   auto wait_copies_and_sync = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
     __syncthreads();
   };
 
-  // Step t of the three-stage pipeline.  On entry `s` holds the (masked)
-  // scores of tile t and `pp` the settled P of tile t-1.  K stage kr holds
-  // tile t+1, V stage vr tile t-1.  The step first waits for the copies of
-  // the previous step, then starts those of tiles t+2 (K, into kw) and t
-  // (V, into vw).  Slot i: scores MFMA i (key block i % 2, d step i / 2) of
-  // tile t+1; p for pairs 4 i .. 4 i + 3 of tile t; P V MFMA of d block i
-  // for tile t-1; e4m3 packs and lane sums of those pairs.
-  auto step = [&](int t, f32x16_t (&s)[2], i32x8_t& pp, int& e_pp,
-                  const uint4* kr, const uint4* vr, const uint4* kw,
-                  const uint4* vw, auto pv_tag) {
-    constexpr bool PV = decltype(pv_tag)::value;
-    const auto rk = rsrc_at(kp, (t + 2) * BT);
-    const auto rv = rsrc_at(vp, t * BT);
-    wait_copies_and_sync();
+  // Scores of tile t from stage ks, masked where needed.
+  // Operand fragments are read one product ahead (the three waves of a
+  // SIMD cover the rest of the LDS latency), which bounds the registers
+  // they take to two fragments.
+  auto scores = [&](int t, const uint4* ks, f32x16_t (&s)[2]) {
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+    i32x8_t kf = kfrag(ks, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8_t kcur = kf;
+      if (i + 1 < 4) kf = kfrag(ks, (i + 1) & 1, (i + 1) >> 1);
+      s[i & 1] = mfma_f8(kcur, qf[i >> 1], s[i & 1]);
+      asm volatile("" ::: "memory");
+    }
+    if (masked_at(t)) apply_mask(s, t * BT);
+  };
+  // Lane-dependent A operand of the row-sum product (see above).
+  const int m16 = lane & 15;
+  const int one = ((m16 == 0 && (lane & 16) == 0) ||
+                   (m16 == 1 && (lane & 16) != 0))
+                      ? 0x38383838
+                      : 0;
+  // P of tile t from its scores (E already settled), its row sums and
+  // O += P V from stage vs.
+  auto accumulate = [&](const f32x16_t (&s)[2], const uint4* vs) {
     const float moff = P_SHIFT - (m0 + static_cast<float>(e_cur));
-    const int eb = 127 + e_pp;          // 2^E of the P being multiplied
-    i32x8_t kf = kfrag(kr, 0, 0);
-    i32x8_t vf;
-    if constexpr (PV) vf = vfrag(vr, 0);
-    f32x16_t sn[2];
-    sn[0] = f32x16_t{};
-    sn[1] = f32x16_t{};
-    // Packed P words: each is written as its low half, then its high half,
-    // so its starting contents do not matter (left undefined, which spares
-    // clearing them).  The lane sums start from the first two pairs.
     int pw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" : "=v"(pw[i]));
     float ls0, ls1;
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8_t kcur = kf;
-      if (i + 1 < 4) kf = kfrag(kr, (i + 1) & 1, (i + 1) >> 1);
-      sn[i & 1] = mfma_f8(kcur, qf[i >> 1], sn[i & 1]);
-      // Copies spread over the slots: V window i / 2 on even slots, K window
-      // i / 2 on odd ones.
-      if (i / 2 < NWIN) {
-        const int w = i / 2;
-        if (i % 2 == 0)
-          copy_to_lds(rv, vw + 64 * (wave + NWAVE * w), voff + w * WIN_BYTES);
-        else
-          copy_to_lds(rk, kw + 64 * (wave + NWAVE * w), koff + w * WIN_BYTES);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      float e[4][2];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int pr = 4 * i + q;
-        const int kb = pr >> 3, r = 2 * (pr & 7);
-        e[q][0] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
-        e[q][1] = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
-        asm volatile("" : "+v"(e[q][0]), "+v"(e[q][1]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (PV) {
-        const i32x8_t vcur = vf;
-        if (i + 1 < 4) vf = vfrag(vr, i + 1);
-        oacc[i] = mfma_f8_bscale(vcur, pp, oacc[i], eb);
-        // Keeps the product in its slot: without a use here the compiler
-        // sinks all four past the masking branch, after the exps.
-        asm volatile("" : "+v"(oacc[i]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int pr = 4 * i + q;
-        pw[pr >> 1] = pack_fp8x2(e[q][0], e[q][1], pw[pr >> 1], pr & 1);
-        float& ls = (q & 1) ? ls1 : ls0;
-        if (pr < 2)
-          ls = e[q][0] + e[q][1];
-        else
-          ls += e[q][0] + e[q][1];
-        asm volatile("" : "+v"(pw[pr >> 1]), "+v"(ls));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 16; ++q) {
+      const int kb = q >> 3, r = 2 * (q & 7);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
+      pw[q >> 1] = pack_fp8x2(e0, e1, pw[q >> 1], q & 1);
+      float& ls = (q & 1) ? ls1 : ls0;
+      if (q < 2)
+        ls = e0 + e1;
+      else
+        ls += e0 + e1;
+      // Each pair is packed and summed before the next is formed (keeps
+      // the live registers to one pair).
+      asm volatile("" : "+v"(pw[q >> 1]), "+v"(ls));
     }
-    // O is divided by the sum of the rounded values the P V product used,
-    // so a row whose weight sits on one key still divides that key's value
-    // by itself; l (fp32 p before rounding) gives the LSE.
-    if constexpr (PV) lacc = mfma_f8_bscale(ones, pp, lacc, eb);
+    asm volatile("" ::: "memory");
+    const i32x8_t pp = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    const int eb = 127 + e_cur;
+    const i32x8_t ones = {one, one, one, one, one, one, one, one};
+    // A fresh accumulator per tile (a large running C would be added to the
+    // 64 products with the matrix core's own alignment); fp32 sums after.
+    f32x4_t lt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        ones, pp, f32x4_t{}, 0, 0, 0, 127, 0, 127);
+    asm volatile("" : "+v"(lt));
+    lraw0 += lt[0];
+    lraw1 += lt[1];
+    i32x8_t vf = vfrag(vs, 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i32x8_t vcur = vf;
+      if (db + 1 < 4) vf = vfrag(vs, db + 1);
+      oacc[db] = mfma_f8_bscale(vcur, pp, oacc[db], eb);
+      // Keeps the product here (the compiler would otherwise sink the four
+      // of them into the next tile, keeping V and P live across it).
+      asm volatile("" : "+v"(oacc[db])::"memory");
+    }
     l_run += __builtin_ldexpf(ls0 + ls1, e_cur);
-    pp = i32x8_t{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    e_pp = e_cur;
-    if (masked_at(t + 1)) apply_mask(sn, (t + 1) * BT);
-    s[0] = sn[0];
-    s[1] = sn[1];
-    // E changes only for a row whose maximum passes over() > E, which one
-    // of the row's two lanes sees alone; the exchange between lane halves
-    // and the update run only when some lane sees it (rare: E never falls).
+  };
+  // E for a tile with these scores (the smallest integer, never falling,
+  // that keeps the row maximum within P_HEADROOM of m0 + E); O, l and the
+  // row sums move down by 2^E if E passes E_RENORM.
+  // Folds the raw row sums into the totals at the current E (lane n < 16:
+  // E of query n is its own, that of query n + 16 is lane n + 16's).
+  auto fold_lq = [&]() {
+    const int e_hi = __builtin_amdgcn_ds_bpermute(((lane & 15) + 16) << 2,
+                                                  e_cur);
+    lq0 += __builtin_ldexpf(lraw0, e_cur);
+    lq1 += __builtin_ldexpf(lraw1, e_hi);
+    lraw0 = 0.f;
+    lraw1 = 0.f;
+  };
+  auto settle_e = [&](const f32x16_t (&s)[2]) {
     const float lmx = lane_max(s);
     if (__builtin_amdgcn_ballot_w64(over(lmx) > static_cast<float>(e_cur)) !=
         0) {
+      fold_lq();
       e_cur = next_e(half_max(lmx), e_cur);
       if (__builtin_amdgcn_ballot_w64(e_cur > E_RENORM) != 0) {   // rare
-        // Move the base up by E: O, l and the pending P's scale follow.
+        // Every row moves its base up by its own E; lq1 (lane n < 16)
+        // belongs to query n + 16, whose E is lane n + 16's.
         const int sh = e_cur;
+        const int sh_hi =
+            __builtin_amdgcn_ds_bpermute(((lane & 15) + 16) << 2, sh);
         const float f = __builtin_ldexpf(1.0f, -sh);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
         l_run *= f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lacc[r] *= f;
+        lq0 *= f;
+        lq1 = __builtin_ldexpf(lq1, -sh_hi);
         m0 += static_cast<float>(sh);
-        e_pp = max(e_pp - sh, -127);
         e_cur = 0;
       }
     }
   };
 
-  // ---- prologue: K tiles 0 and 1 into LDS, scores of tile 0 ----
-  // Stages: tile u lives in Ks[u % 2] / Vs[u % 2]; step t reads K(t+1) and
-  // V(t-1), both from stage (t+1) % 2, and fills stage t % 2.
-#pragma unroll
-  for (int w = 0; w < NWIN; ++w) {
-    copy_to_lds(rsrc_at(kp, 0), Ks0 + 64 * (wave + NWAVE * w),
-                koff + w * WIN_BYTES);
-    copy_to_lds(rsrc_at(kp, BT), Ks1 + 64 * (wave + NWAVE * w),
-                koff + w * WIN_BYTES);
+  // Stages: tile t lives in Ks[t % 2] / Vs[t % 2].  Tiles 0 and 1 come
+  // first, then pairs (t, t + 1) for even t; when the tile count is odd the
+  // last pair's second tile (or tile 1 when there is one tile) is virtual:
+  // its copies read zeros (the descriptors end at kv_end) and its scores are
+  // masked, so its p are 0.  Every copy issued is waited for before its
+  // tile is read, so none is in flight when the workgroup ends.
+  copy_tile(0, Ks0, Vs0);
+  wait_copies_and_sync();
+  copy_tile(1, Ks1, Vs1);
+  {
+    // Tile 0 sets the base (every row sees key 0: finite for existing rows).
+    f32x16_t s[2];
+    scores(0, Ks0, s);
+    const float mx = half_max(lane_max(s));
+    m0 = (mx == -__builtin_inff()) ? 0.f : mx * c;
+    accumulate(s, Vs0);
   }
   wait_copies_and_sync();
-  f32x16_t s[2];
-  s[0] = f32x16_t{};
-  s[1] = f32x16_t{};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    s[i & 1] = mfma_f8(kfrag(Ks0, i & 1, i >> 1), qf[i >> 1], s[i & 1]);
-  if (masked_at(0)) apply_mask(s, 0);
+  if (2 < ntiles) copy_tile(2, Ks0, Vs0);
   {
-    // Base from tile 0 (every row sees key 0, so it is finite for the rows
-    // that exist).
-    const float mx = tile_max(s);
-    m0 = (mx == -__builtin_inff()) ? 0.f : mx * c;
+    f32x16_t s[2];
+    scores(1, Ks1, s);
+    settle_e(s);
+    accumulate(s, Vs1);
   }
-  i32x8_t pp = {};
-  int e_pp = 0;
-
-  step(0, s, pp, e_pp, Ks1, Vs1, Ks0, Vs0, Tag<false>{});
-  for (int t = 1; t <= nsteps; t += 2) {
-    step(t, s, pp, e_pp, Ks0, Vs0, Ks1, Vs1, Tag<true>{});
-    step(t + 1, s, pp, e_pp, Ks1, Vs1, Ks0, Vs0, Tag<true>{});
+  for (int t = 2; t < ntiles; t += 2) {
+    wait_copies_and_sync();
+    copy_tile(t + 1, Ks1, Vs1);
+    {
+      f32x16_t s[2];
+      scores(t, Ks0, s);
+      settle_e(s);
+      accumulate(s, Vs0);
+    }
+    wait_copies_and_sync();
+    if (t + 2 < ntiles) copy_tile(t + 2, Ks0, Vs0);
+    {
+      f32x16_t s[2];
+      scores(t + 1, Ks1, s);
+      settle_e(s);
+      accumulate(s, Vs1);
+    }
   }
 
-  // Epilogue.  Accumulator row m <-> d = 32 db + m: lane half h holds runs
-  // of 4 consecutive d at 32 db + 8 (r / 4) + 4 h.
-  // O divides by the sum of the weights it was built from (the e4m3 values);
-  // the LSE takes the sum of the unrounded p.
+  // Epilogue.  Lane n < 16 holds the totals of queries n and n + 16; lane
+  // L needs that of query L % 32.
+  fold_lq();
   const float l_tot = half_sum(l_run);
-  const float lq_tot = lacc[0];
+  const int src = (li & 15) << 2;
+  const float lqa = __int_as_float(
+      __builtin_amdgcn_ds_bpermute(src, __float_as_int(lq0)));
+  const float lqb = __int_as_float(
+      __builtin_amdgcn_ds_bpermute(src, __float_as_int(lq1)));
+  const float lq_tot = (li < 16) ? lqa : lqb;
   const float inv = (lq_tot > 0.f) ? dv / lq_tot : 0.f;
   if (qrow < N) {
     uint16_t* op = static_cast<uint16_t*>(a.o) +
@@ -529,30 +520,23 @@ fwd_fp8_kernel(const FwdArgs a) {
 
 }  // namespace
 
-template <int NWAVE>
-hipError_t launch_waves(FwdArgs a, bool causal, hipStream_t stream) {
-  constexpr int BR = 32 * NWAVE;
+hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
+  constexpr int BR = 128;
   a.nqb = (a.N + BR - 1) / BR;
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  // Per-(batch, KV head) byte ranges are addressed by 32-bit buffer
-  // offsets.
   if (static_cast<long long>(a.N) * D > 0x7FFFFFFFLL)
     return hipErrorInvalidConfiguration;
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
   if (causal) {
-    hipLaunchKernelGGL((fwd_fp8_kernel<true, NWAVE>), dim3((int)grid),
-                       dim3(64 * NWAVE), 0, stream, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3((int)grid),
+                       dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((fwd_fp8_kernel<false, NWAVE>), dim3((int)grid),
-                       dim3(64 * NWAVE), 0, stream, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<false>), dim3((int)grid),
+                       dim3(256), 0, stream, a);
   }
   return hipGetLastError();
-}
-
-hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
-  return launch_waves<NWAVE_FP8>(a, causal, stream);
 }
 
 }  // namespace fa
