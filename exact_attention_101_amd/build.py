@@ -12,6 +12,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
+# Race-check build of the same sources: every tile copy of the forward
+# kernels serialised behind barriers (FA_SERIAL_COPIES, fa_common.h).
+SERIAL_LIB = os.path.join(HERE, "libfa_serial.so")
 # Issue-rate probes of the SIMD (measurement support, its own library).
 PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
 PROBE_SOURCES = ["fa_probe_rates.hip"]
@@ -64,11 +67,52 @@ def _compile(out: str, sources, extra=(), verbose: bool = False) -> str:
     return out
 
 
+ROOT = os.path.dirname(HERE)
+# Host-side C-ABI driver under AddressSanitizer and UndefinedBehaviorSanitizer
+# (CPU only: every call it makes is rejected before reaching the GPU).  The
+# sanitizers instrument the host pass only.
+SANITIZE_DRIVER = os.path.join(ROOT, "tests", "cabi_sanitize_driver.cpp")
+SANITIZE_BIN = os.path.join(ROOT, "tests", "_build", "cabi_sanitize")
+SANITIZE_FLAGS = [
+    "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Compile the sanitised C-ABI driver with every library source."""
+    os.makedirs(os.path.dirname(SANITIZE_BIN), exist_ok=True)
+    srcs = [SANITIZE_DRIVER] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [HIPCC, *SANITIZE_FLAGS, "-o", SANITIZE_BIN + ".tmp", *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    os.replace(SANITIZE_BIN + ".tmp", SANITIZE_BIN)
+    return SANITIZE_BIN
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libfa.so, and the probe library
-    (always rebuilds)."""
-    _compile(LIB, SOURCES, verbose=verbose)
-    _compile(PROBE_LIB, PROBE_SOURCES, verbose=verbose)
+    """Compile every HIP source into libfa.so, the race-check build of the
+    same sources, the probe library and the sanitised C-ABI driver (always
+    rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [
+        lambda: _compile(LIB, SOURCES, verbose=verbose),
+        lambda: _compile(SERIAL_LIB, SOURCES, extra=["-DFA_SERIAL_COPIES=1"],
+                         verbose=verbose),
+        lambda: _compile(PROBE_LIB, PROBE_SOURCES, verbose=verbose),
+        lambda: build_sanitized(verbose=verbose),
+    ]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as pool:
+        for f in [pool.submit(j) for j in jobs]:
+            f.result()
     return LIB
 
 

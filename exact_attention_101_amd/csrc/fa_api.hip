@@ -38,6 +38,13 @@ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// a * b * c > limit, for positive ints, without overflowing (the product of
+// three ints can pass 2^63).
+bool product_exceeds(int a, int b, int c, long long limit) {
+  const long long ab = static_cast<long long>(a) * b;   // < 2^62
+  return ab > limit / c;
+}
+
 // Checks shared by both forward entry points, in the documented order.
 int check_fwd(const void* q, const void* k, const void* v, const void* o,
               const void* lse, int B, int H, int Hkv, int N, int d,
@@ -50,8 +57,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
   // Element counts must fit comfortably in 64 bits; B*H*N must fit in int
   // arithmetic on the device side (per-head offsets are 64-bit).
-  const long long bhn = static_cast<long long>(B) * H * N;
-  if (bhn > (1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
+  if (product_exceeds(B, H, N, 1LL << 40)) return FA_ERR_INVALID_ARGUMENT;
   if (!d_ok) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       !aligned16(lse))
@@ -166,8 +172,8 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
   if (H % Hkv != 0 || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
   if (num_splits < 1 || num_splits > fa::SPLITKV_MAX_SPLITS)
     return FA_ERR_INVALID_ARGUMENT;
-  if (static_cast<long long>(B) * H * Nq > (1LL << 40) ||
-      static_cast<long long>(B) * Hkv * Nk > (1LL << 40))
+  if (product_exceeds(B, H, Nq, 1LL << 40) ||
+      product_exceeds(B, Hkv, Nk, 1LL << 40))
     return FA_ERR_INVALID_ARGUMENT;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -272,6 +278,9 @@ FA_EXPORT int fa_fwd_masked(const void* q, const void* k, const void* v,
     return FA_ERR_INVALID_ARGUMENT;
   if (H % Hkv != 0 || !isfinite(scale) || mask_batch_stride < 0 ||
       mask_head_stride < 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (product_exceeds(B, H, Nq, 1LL << 40) ||
+      product_exceeds(B, Hkv, Nk, 1LL << 40))
     return FA_ERR_INVALID_ARGUMENT;
   if (d != 128 || Nk > fa::MASK_MAX_NK) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||

@@ -338,8 +338,8 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream) {
   const long long rows = static_cast<long long>(a.B) * a.H * a.N;
   const long long prep_grid = (rows + 15) / 16;
-  a.nqb = (a.N + BLK - 1) / BLK;
-  a.nkb = (a.N + BLK - 1) / BLK;
+  a.nqb = static_cast<int>((static_cast<long long>(a.N) + BLK - 1) / BLK);
+  a.nkb = a.nqb;
   const long long dq_grid = static_cast<long long>(a.B) * a.H * a.nqb;
   const long long kv_grid = static_cast<long long>(a.B) * a.Hkv * a.nkb;
   if (prep_grid > 0x7FFFFFFFLL || dq_grid > 0x7FFFFFFFLL ||

@@ -5,7 +5,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Race-check build (-DFA_SERIAL_COPIES=1, libfa_serial.so): the forward
+// kernels put a workgroup barrier before every batch of tile copies into
+// LDS and wait for the copies and meet at a barrier again right after it,
+// so no stage is read while a copy into it is in flight and none is
+// overwritten while a wave may still read it.  Its outputs must equal the
+// pipelined build's bit for bit; a difference is a synchronisation bug.
+#ifndef FA_SERIAL_COPIES
+#define FA_SERIAL_COPIES 0
+#endif
+
 namespace fa {
+
+constexpr bool SERIAL_COPIES = FA_SERIAL_COPIES != 0;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;

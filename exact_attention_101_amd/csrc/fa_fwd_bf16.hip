@@ -688,7 +688,13 @@ fwd_bf16_kernel(const FwdArgs a) {
           rk = rsrc_at(kp, (tile + 2) * BT);
           rv = rsrc_at(vp, (tile + 1) * BT);
         }
+        if constexpr (SERIAL_COPIES) {
+          if (i == 1) wait_copies_and_sync();
+        }
         if (i >= 1 && i <= NCOPY) copy_nth(i - 1, rk, rv, kw, vw);
+        if constexpr (SERIAL_COPIES) {
+          if (i == NCOPY) wait_copies_and_sync();
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       float e[PPS][2];
@@ -888,7 +894,7 @@ static hipError_t launch(const FwdArgs& a, int grid, hipStream_t stream) {
 // template with 8 waves of 32 rows, per-sequence offsets and window
 // masks.  a.nqb covers the longest query sequence.
 hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream) {
-  a.nqb = (max_q + BR - 1) / BR;
+  a.nqb = static_cast<int>((static_cast<long long>(max_q) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   if (static_cast<long long>(a.total_k) * 128 * 2 > 0x7FFFFFFFLL)
@@ -900,7 +906,7 @@ hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
-  a.nqb = (a.N + BR - 1) / BR;
+  a.nqb = static_cast<int>((static_cast<long long>(a.N) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   // Per-(batch, KV head) byte ranges are addressed by 32-bit buffer

@@ -450,6 +450,7 @@ fwd_fp8_kernel(const FwdArgs a) {
   copy_tile(0, Ks0, Vs0);
   wait_copies_and_sync();
   copy_tile(1, Ks1, Vs1);
+  if constexpr (SERIAL_COPIES) wait_copies_and_sync();
   {
     // Tile 0 sets the base (every row sees key 0: finite for existing rows).
     f32x16_t s[2];
@@ -460,6 +461,7 @@ fwd_fp8_kernel(const FwdArgs a) {
   }
   wait_copies_and_sync();
   if (2 < ntiles) copy_tile(2, Ks0, Vs0);
+  if constexpr (SERIAL_COPIES) wait_copies_and_sync();
   {
     f32x16_t s[2];
     scores(1, Ks1, s);
@@ -469,6 +471,7 @@ fwd_fp8_kernel(const FwdArgs a) {
   for (int t = 2; t < ntiles; t += 2) {
     wait_copies_and_sync();
     copy_tile(t + 1, Ks1, Vs1);
+    if constexpr (SERIAL_COPIES) wait_copies_and_sync();
     {
       f32x16_t s[2];
       scores(t, Ks0, s);
@@ -477,6 +480,7 @@ fwd_fp8_kernel(const FwdArgs a) {
     }
     wait_copies_and_sync();
     if (t + 2 < ntiles) copy_tile(t + 2, Ks0, Vs0);
+    if constexpr (SERIAL_COPIES) wait_copies_and_sync();
     {
       f32x16_t s[2];
       scores(t + 1, Ks1, s);
@@ -522,7 +526,7 @@ fwd_fp8_kernel(const FwdArgs a) {
 
 hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
   constexpr int BR = 128;
-  a.nqb = (a.N + BR - 1) / BR;
+  a.nqb = static_cast<int>((static_cast<long long>(a.N) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   if (static_cast<long long>(a.N) * D > 0x7FFFFFFFLL)

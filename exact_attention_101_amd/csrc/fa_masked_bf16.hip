@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(NTHR, 1) masked_kernel(const MaskArgs a) {
 
 hipError_t launch_masked_bf16(MaskArgs a, hipStream_t stream) {
   a.W = (a.Nk + T - 1) / T;
-  a.nqb = (a.Nq + BLK - 1) / BLK;
+  a.nqb = static_cast<int>((static_cast<long long>(a.Nq) + BLK - 1) / BLK);
   const long long grid = static_cast<long long>(a.nqb) * a.H * a.B;
   if (grid > 0x7FFFFFFFLL || a.Nk > MASK_MAX_NK)
     return hipErrorInvalidConfiguration;

@@ -370,8 +370,11 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(const SplitArgs a) {
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk) {
   const long long rows = static_cast<long long>(Nq) * (H / Hkv);
   const long long nrb = (rows + T - 1) / T;
-  const long long units = static_cast<long long>(B) * Hkv * nrb;
-  const long long nkb = (Nk + T - 1) / T;
+  // B * Hkv * nrb can pass 2^63 for sizes at the int limits; only whether it
+  // reaches 1024 matters.
+  const long long bk = static_cast<long long>(B) * Hkv;
+  const long long units = (bk >= 1024 || nrb >= 1024) ? 1024 : bk * nrb;
+  const long long nkb = (static_cast<long long>(Nk) + T - 1) / T;
   // About 1024 waves, one round at this kernel's 5 waves per CU, each split
   // at least 4 tiles.  Measured on decode shapes against 1280, 2048 and 2560
   // waves: best or tied everywhere (two rounds leave a tail, and split

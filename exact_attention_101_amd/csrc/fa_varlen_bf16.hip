@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(NTHR, 1) varlen_kernel(const VarlenArgs a) {
 }  // namespace
 
 hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream) {
-  a.nqb = (a.max_q + BLK - 1) / BLK;
+  a.nqb = static_cast<int>((static_cast<long long>(a.max_q) + BLK - 1) / BLK);
   const long long grid = static_cast<long long>(a.nqb) * a.H * a.B;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   if (static_cast<long long>(a.total_k) * D * 2 > 0x7FFFFFFFLL)

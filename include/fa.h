@@ -88,7 +88,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Hopper»: tensor X is represented by codes x8 and a descale factor
  * delta_X with X ~= decode(x8) * delta_X.
  *   q8, k8, v8   device e4m3 codes, layouts as above.
- *   o, lse       as for fa_fwd (o is bfloat16).
+ *   o, lse       as for fa_fwd (o is bfloat16).  lse is formed from the
+ *                unrounded fp32 weights, but the e4m3 matrix cores do not
+ *                add their 64 products exactly in fp32 (a product is
+ *                truncated to the alignment of the largest in its group of
+ *                eight), so a score next to an outlier product is off by
+ *                about 2^-14 of that product: |lse - exact| stays within
+ *                5e-2 on inputs with 0.1% outliers x20 (about 1e-3
+ *                without outliers).
  *   descale_qkv  device float[3] = {delta_Q, delta_K, delta_V}, read by the
  *                kernel (no host synchronisation), or NULL for {1, 1, 1}.
  *   d            must be 128.  Other arguments as for fa_fwd.
@@ -185,9 +192,14 @@ int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk);
  *             [cu[b], cu[b+1]).  Read by the kernel: a sequence whose rows
  *             fall outside [0, total) is skipped and its outputs are left
  *             unwritten.
- *   max_seqlen_q  at least the longest query sequence (rows beyond it are
- *             not computed).
- *   window_left, window_right  >= -1 (-1 = unbounded).
+ *   max_seqlen_q  the longest query sequence (the grid is sized from it;
+ *             the library cannot read cu_seqlens_q without a synchronisation).
+ *             A smaller value computes each sequence's rows below it; rows
+ *             at or past it rounded up to a multiple of 256 are not written.
+ *   total_q, total_k  at most 2^29 (FA_ERR_INVALID_ARGUMENT above).
+ *   window_left, window_right  >= -1 (-1 = unbounded); any width reaching
+ *             past every sequence (window_left >= total_k, window_right >=
+ *             total_q) is the unbounded window.
  *   d must be 128; H, Hkv, scale as for fa_fwd.  Errors as for fa_fwd;
  *   lse and the cu_seqlens arrays need 4-byte alignment.  One kernel is
  *   enqueued on `stream`.

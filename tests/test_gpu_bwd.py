@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import dev
+from gpu_helpers import block_rows, dev, nan_filled
 
 pytestmark = pytest.mark.gpu
 
@@ -88,14 +88,25 @@ def test_bwd_causal_gqa_medium():
     _compare(got, want, "causal gqa 1000")
 
 
-def test_bwd_full_size_sampled():
-    """The headline shape (B4 H16 N8192 d128, non-causal): sampled query rows
-    (dQ) and key rows (dK, dV) of sampled heads."""
+def test_bwd_full_size_every_head():
+    """The headline shape (B4 H16 N8192 d128, non-causal): every KV head, at
+    one random row of every 128-row block plus the boundary rows, for dQ
+    (every query head of the group) and for dK, dV.  The gradients start as
+    NaN, so a block the launches never write fails."""
+    import torch
+    import exact_attention_101_amd as fa
     w = workloads.WORKLOADS[workloads.HEADLINE]
     tb, vals = _inputs(w.B, w.H, w.Hkv, w.N, w.d, 9700)
-    got = _gpu_backward(tb, w.causal)
-    rows = np.array([0, 1, 127, 128, 4095, 8063, 8191])
-    kv_heads = [(0, 0), (w.B - 1, w.Hkv - 1)]
+    q, k, v, do = (t.to(dev()) for t in tb)
+    o, lse = fa.forward(q, k, v, causal=w.causal)
+    dq, dk, dv = (nan_filled(t.shape, torch.bfloat16) for t in (q, k, v))
+    fa.backward(q, k, v, o, lse, do, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    for g in got:
+        assert np.all(np.isfinite(g))
+    rows = block_rows(w.N, 128, np.random.default_rng(9701))
+    kv_heads = [(b, kvh) for b in range(w.B) for kvh in range(w.Hkv)]
     sq, sk, sv = oracle.attention_backward_sampled(*vals, rows, rows, kv_heads,
                                                    causal=w.causal)
     g = w.H // w.Hkv
@@ -103,7 +114,7 @@ def test_bwd_full_size_sampled():
                    for b, kvh in kv_heads])
     gk = np.stack([got[1][b, kvh][rows] for b, kvh in kv_heads])
     gv = np.stack([got[2][b, kvh][rows] for b, kvh in kv_heads])
-    _compare((gq, gk, gv), (sq, sk, sv), "headline sampled")
+    _compare((gq, gk, gv), (sq, sk, sv), "headline, every KV head")
 
 
 def test_bwd_deterministic():

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import FP8_REL_L2_TOL, LSE_TOL, dev, sample_heads, sample_rows
+from gpu_helpers import (FP8_LSE_TOL, FP8_REL_L2_TOL, block_rows, dev,
+                         nan_filled)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,27 +86,65 @@ def test_fp8_small_full(shape, causal, rotate):
     assert rel <= FP8_REL_L2_TOL
 
 
-@pytest.mark.parametrize("rotate", [False, True])
-def test_fp8_full_size_sampled(rotate):
-    """The fp8 workload at full size; sampled rows of sampled heads against
-    the oracle on the oracle's own dequantised inputs.  Also reports (not
-    gated) the error against the unquantised inputs."""
-    w = workloads.WORKLOADS["fp8_n8192"]
+def _fp8_full_size(w, signs):
+    """The fp8 workload through the benchmark's launch, O and LSE starting
+    as NaN; returns the outputs and the oracle's dequantised inputs."""
+    import torch
+    import exact_attention_101_amd as fa
     q, k, v = workloads.workload_qkv(w)
-    signs = workloads.hadamard_signs(w.d, w.seed(9)) if rotate else None
-    o, lse = _fp8_forward(q, k, v, signs, w.causal)
-    rows = sample_rows(w.N, w.index, n_random=8)
-    heads = sample_heads(w.B, w.H, w.index, n=4)
-    qd, kd, vd = _oracle_deq(q, signs), _oracle_deq(k, signs), _oracle_deq(v, None)
-    ro, rl = oracle.attention_rows(qd, kd, vd, rows, heads=heads)
-    go = np.stack([o[b, h][rows] for b, h in heads])
-    rel = np.linalg.norm(go - ro) / np.linalg.norm(ro)
-    exact, _ = oracle.attention_rows(q, k, v, rows, heads=heads)
-    rel_exact = np.linalg.norm(go - exact) / np.linalg.norm(exact)
-    print(f"fp8 rotate={rotate}: rel-L2 vs dequantised oracle {rel:.3e}; "
-          f"vs unquantised inputs {rel_exact:.3e}")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    assert rel <= FP8_REL_L2_TOL
+    q8, sq = _quant(q, signs)
+    k8, sk = _quant(k, signs)
+    v8, sv = _quant(v, None)
+    desc = torch.stack([sq[1], sk[1], sv[1]]).contiguous()
+    o_t = nan_filled((w.B, w.H, w.N, w.d), torch.bfloat16)
+    l_t = nan_filled((w.B, w.H, w.N), torch.float32)
+    fa.forward_fp8(q8, k8, v8, desc, causal=w.causal, out=o_t, lse=l_t)
+    torch.cuda.synchronize()
+    deq = (_oracle_deq(q, signs), _oracle_deq(k, signs), _oracle_deq(v, None))
+    return o_t.float().cpu().numpy(), l_t.cpu().numpy(), (q, k, v), deq
+
+
+def test_fp8_full_size_every_block():
+    """The fp8 workload at full size, both variants (with and without the
+    Hadamard rotation of Q and K).  Every (batch, head) is compared with the
+    oracle on its own dequantised inputs on one random row of every 128-row
+    query block plus the boundary rows (O: rel-L2 over all of them; LSE:
+    FP8_LSE_TOL).  Also measured against the oracle on the unquantised
+    inputs: the rotation must lower that error (the direction of the
+    FlashAttention-3 summary's claim, section «Baixa precisão»; the size of
+    the gain depends on the input distribution, which the pages do not
+    give)."""
+    w = workloads.WORKLOADS["fp8_n8192"]
+    exact_err = {}
+    for rotate in (False, True):
+        signs = workloads.hadamard_signs(w.d, w.seed(9)) if rotate else None
+        o, lse, (q, k, v), (qd, kd, vd) = _fp8_full_size(w, signs)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        rng = np.random.default_rng(w.index)
+        num = den = num_x = den_x = 0.0
+        el = 0.0
+        for b in range(w.B):
+            for h in range(w.H):
+                rows = block_rows(w.N, 128, rng)
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                ro, rl = oracle.attention_rows(qd[sl], kd[sl], vd[sl], rows)
+                go = o[b, h][rows]
+                num += float(np.sum((go - ro[0]) ** 2))
+                den += float(np.sum(ro[0] ** 2))
+                el = max(el, float(np.abs(lse[b, h][rows] - rl[0]).max()))
+                rx, _ = oracle.attention_rows(q[sl], k[sl], v[sl], rows)
+                num_x += float(np.sum((go - rx[0]) ** 2))
+                den_x += float(np.sum(rx[0] ** 2))
+        rel = (num / den) ** 0.5
+        exact_err[rotate] = (num_x / den_x) ** 0.5
+        print(f"fp8 rotate={rotate}: rel-L2 vs dequantised oracle {rel:.3e}, "
+              f"max|dLSE| {el:.3e}; vs unquantised inputs "
+              f"{exact_err[rotate]:.3e}")
+        assert rel <= FP8_REL_L2_TOL, rel
+        assert el <= FP8_LSE_TOL, el
+    print(f"fp8 error against the unquantised inputs, unrotated / rotated: "
+          f"{exact_err[False] / exact_err[True]:.2f}x")
+    assert exact_err[True] < exact_err[False]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -140,4 +179,4 @@ def test_fp8_reference_moves(case, causal):
     print(f"fp8 {case}: rel-L2={rel:.3e} max|dLSE|={el:.3e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert rel <= FP8_REL_L2_TOL
-    assert el <= 2e-2
+    assert el <= FP8_LSE_TOL
