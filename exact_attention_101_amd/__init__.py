@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_kv", "forward_varlen", "forward_masked", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "forward_kv", "forward_kv_noalloc", "forward_varlen", "forward_masked", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -31,6 +31,7 @@ FA_ERR_INVALID_ARGUMENT = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_MISALIGNED = 3
 FA_ERR_HIP = 4
+FA_ERR_WORKSPACE = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfa.so")
@@ -64,6 +65,10 @@ def library() -> ctypes.CDLL:
         lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
                                        i32, i32, i32, i32, f32, i32, vp, vp]
         lib.fa_fwd_splitkv.restype = i32
+        lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32,
+                                               i32, i32, i32, i32, i32, f32,
+                                               i32, vp]
+        lib.fa_fwd_splitkv_noalloc.restype = i32
         lib.fa_splitkv_num_splits.argtypes = [i32, i32, i32, i32, i32]
         lib.fa_splitkv_num_splits.restype = i32
         lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32,
@@ -201,6 +206,38 @@ def forward_kv(q, k, v, *, causal: bool = False, scale=None, num_splits=None,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
         int(num_splits), workspace.data_ptr(), _stream_handle(q.device)))
+    return out, lse
+
+
+def forward_kv_noalloc(q, k, v, out, lse, *, causal: bool = False,
+                       scale=None, num_splits=None):
+    """forward_kv for callers that cannot allocate (graph capture, serving
+    loops): the caller passes out and lse, and the splits' partial results
+    go to the library's fixed per-device scratch (fa_fwd_splitkv_noalloc), so
+    nothing is allocated.  Sizes whose num_splits * B * H * Nq * (d + 1)
+    exceed that scratch raise ValueError; calls that overlap on one GPU
+    race."""
+    import torch
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or \
+                t.dtype != torch.bfloat16 or t.device != q.device:
+            raise ValueError("forward_kv_noalloc expects contiguous 4-D "
+                             "bfloat16 tensors on one GPU")
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, dk = k.shape
+    if k.shape != v.shape or k.shape[0] != B or dk != d:
+        raise ValueError("k/v shape does not match q")
+    _out_check(out, "out", q.shape, torch.bfloat16, q.device)
+    _out_check(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    lib = library()
+    if num_splits is None:
+        num_splits = lib.fa_splitkv_num_splits(B, H, Hkv, Nq, Nk) or 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd_splitkv_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+        int(num_splits), _stream_handle(q.device)))
     return out, lse
 
 

@@ -14,6 +14,7 @@ hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
+hipError_t splitkv_scratch(float** out);
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
 hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream);
 hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream);
@@ -161,12 +162,14 @@ FA_EXPORT int fa_splitkv_num_splits(int B, int H, int Hkv, int Nq, int Nk) {
   return fa::splitkv_auto_splits(B, H, Hkv, Nq, Nk);
 }
 
-FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
-                             void* o, float* lse, int B, int H, int Hkv,
-                             int Nq, int Nk, int d, int causal, float scale,
-                             int num_splits, float* workspace, void* stream) {
-  if (!q || !k || !v || !o || !lse || !workspace)
-    return FA_ERR_INVALID_ARGUMENT;
+namespace {
+
+// Checks shared by the two split-KV entry points, in the documented order
+// (the workspace pointer, when there is one, is checked by the caller).
+int check_splitkv(const void* q, const void* k, const void* v, const void* o,
+                  const void* lse, int B, int H, int Hkv, int Nq, int Nk,
+                  int d, float scale, int num_splits) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
     return FA_ERR_INVALID_ARGUMENT;
   if (H % Hkv != 0 || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
@@ -177,8 +180,14 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
     return FA_ERR_INVALID_ARGUMENT;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      !aligned16(lse) || !aligned16(workspace))
+      !aligned16(lse))
     return FA_ERR_MISALIGNED;
+  return FA_OK;
+}
+
+int run_splitkv(const void* q, const void* k, const void* v, void* o,
+                float* lse, int B, int H, int Hkv, int Nq, int Nk, int causal,
+                float scale, int num_splits, float* workspace, void* stream) {
   fa::SplitArgs a{};
   a.q = q;
   a.k = k;
@@ -197,6 +206,40 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
   a.ws_lse = workspace + rows * num_splits * 128;
   return hip_status(fa::launch_splitkv_bf16(a, causal != 0,
                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int B, int H, int Hkv,
+                             int Nq, int Nk, int d, int causal, float scale,
+                             int num_splits, float* workspace, void* stream) {
+  if (!workspace) return FA_ERR_INVALID_ARGUMENT;
+  const int st = check_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale,
+                               num_splits);
+  if (st != FA_OK) return st;
+  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  return run_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, causal, scale,
+                     num_splits, workspace, stream);
+}
+
+FA_EXPORT int fa_fwd_splitkv_noalloc(const void* q, const void* k,
+                                     const void* v, void* o, float* lse,
+                                     int B, int H, int Hkv, int Nq, int Nk,
+                                     int d, int causal, float scale,
+                                     int num_splits, void* stream) {
+  const int st = check_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale,
+                               num_splits);
+  if (st != FA_OK) return st;
+  // rows <= 2^40 and num_splits <= 256 after the checks: no overflow.
+  const long long rows = static_cast<long long>(B) * H * Nq;
+  const long long need = rows * num_splits * (d + 1);
+  if (need > fa::SPLITKV_SCRATCH_FLOATS) return FA_ERR_WORKSPACE;
+  float* ws = nullptr;
+  const hipError_t e = fa::splitkv_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return run_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, causal, scale,
+                     num_splits, ws, stream);
 }
 
 FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v,
@@ -347,6 +390,10 @@ FA_EXPORT const char* fa_status_string(int status) {
     case FA_ERR_MISALIGNED:
       return "FA_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch failed";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: num_splits * B * H * Nq * (d + 1) floats do "
+             "not fit in the library's fixed scratch (4194304 floats); pass "
+             "a workspace to fa_fwd_splitkv or use fewer splits";
     default: return "unknown fa status";
   }
 }

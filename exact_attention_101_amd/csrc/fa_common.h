@@ -77,6 +77,9 @@ struct BwdArgs {
 // (fp32, ws_o[s][row][d]) and its log2-unit LSE (ws_lse[s][row]), rows
 // ordered (b, h, query).
 constexpr int SPLITKV_MAX_SPLITS = 256;
+// Floats of the per-device scratch that fa_fwd_splitkv_noalloc uses in place
+// of a caller workspace: num_splits * B * H * Nq * (d + 1) must fit (16 MiB).
+constexpr long long SPLITKV_SCRATCH_FLOATS = 4LL << 20;
 struct SplitArgs {
   const void* q;
   const void* k;

@@ -29,9 +29,21 @@
 // The kernel is bound by HBM: per key it reads 512 bytes of K and V and
 // does 4 d FLOPs per row, so up to 32 rows it stays far below the MFMA
 // ridge.
+#include <mutex>
+
 #include "fa_common.h"
 
 namespace fa {
+
+// Scratch of the entry point that allocates nothing (fa_fwd_splitkv_noalloc):
+// the splits' partial outputs and LSEs, SPLITKV_SCRATCH_FLOATS floats that
+// every GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, not a device address: the device
+// address is taken once per device with hipGetSymbolAddress (with that
+// device current) and only that address is passed to kernels.  All calls on
+// one GPU share its copy; calls that overlap on one GPU race.  Nothing in it
+// needs clearing: every (split, row) entry the merge reads is written first.
+static __device__ __align__(256) float scratch[SPLITKV_SCRATCH_FLOATS];
 
 namespace {
 
@@ -384,6 +396,31 @@ int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk) {
   if (s > cap) s = cap;
   if (s > SPLITKV_MAX_SPLITS) s = SPLITKV_MAX_SPLITS;
   return static_cast<int>(s < 1 ? 1 : s);
+}
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+// Device address of this device's scratch (the current device's), set up on
+// the first call on each device.
+hipError_t splitkv_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream) {

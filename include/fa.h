@@ -20,8 +20,9 @@
  *
  * Conventions shared by every entry point:
  *   - Device pointers are HIP device allocations owned by the caller.  The
- *     library never allocates or frees device memory, never synchronises the
- *     device, and holds no mutable global state; calls are thread-safe.
+ *     library never allocates or frees device memory and never synchronises
+ *     the device; calls are thread-safe.  The only global state is the
+ *     fixed per-device scratch of fa_fwd_splitkv_noalloc (see there).
  *   - Layouts are dense row-major:  q, o: [B][H][N][d];  k, v: [B][Hkv][N][d];
  *     lse: [B][H][N] (float, natural log).  All offsets are 64-bit.
  *   - Grouped-query attention: H must be a multiple of Hkv; query head h
@@ -41,7 +42,9 @@
  *                                unknown dtype;
  *       FA_ERR_MISALIGNED        a tensor pointer not 16-byte aligned;
  *       FA_ERR_HIP               the launch failed (fa_last_hip_error() gives
- *                                the hipError_t).
+ *                                the hipError_t);
+ *       FA_ERR_WORKSPACE         (fa_fwd_splitkv_noalloc only) the sizes do
+ *                                not fit in its fixed scratch.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -60,7 +63,8 @@ typedef enum {
   FA_ERR_INVALID_ARGUMENT = 1,
   FA_ERR_UNSUPPORTED = 2,
   FA_ERR_MISALIGNED = 3,
-  FA_ERR_HIP = 4
+  FA_ERR_HIP = 4,
+  FA_ERR_WORKSPACE = 5
 } fa_status_t;
 
 /*
@@ -164,6 +168,26 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                    float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
                    int causal, float scale, int num_splits, float* workspace,
                    void* stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc): the same kernels and results, with
+ *   the workspace replaced by a fixed scratch that the library holds on
+ *   every GPU it runs on until the process ends (4194304 floats, 16 MiB).
+ *   The call allocates nothing; its first call on a device looks up that
+ *   device's scratch address (hipGetSymbolAddress, no allocation).
+ *   Arguments as for fa_fwd_splitkv without workspace; the current device
+ *   must be the stream's.  num_splits * B * H * Nq * (d + 1) must be at
+ *   most 4194304, else FA_ERR_WORKSPACE (after the other checks, before
+ *   anything is enqueued).  All calls on one GPU share its scratch: calls
+ *   that overlap on one GPU (other streams, other threads) race; calls in
+ *   order on one stream do not.  Nothing in the scratch needs clearing.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v,
+                           void* o, float* lse, int B, int H, int Hkv, int Nq,
+                           int Nk, int d, int causal, float scale,
+                           int num_splits, void* stream);
 
 /*
  * fa_splitkv_num_splits -- the split count fa_fwd_splitkv is tuned for on

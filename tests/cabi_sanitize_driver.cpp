@@ -135,6 +135,20 @@ int main() {
     EXPECT(fa_splitkv_num_splits(1, 6, 4, 1, 4096), 0);
   }
 
+  // ---- fa_fwd_splitkv_noalloc ----
+  EXPECT(fa_fwd_splitkv_noalloc(nullptr, A, A, A, Af, 1, 8, 2, 1, 4096, 128,
+                                1, s, 8, nullptr),
+         FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_splitkv_noalloc(A, A, A, A, Af, BIG, BIG, 1, BIG, 8, 128, 1,
+                                s, 8, nullptr),
+         FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_splitkv_noalloc(A, A, A, A, Af, 2, 16, 4, 512, 4096, 128, 1,
+                                s, 256, nullptr),
+         FA_ERR_WORKSPACE);
+  EXPECT(fa_fwd_splitkv_noalloc(A, A, A, A, Af, 1 << 20, 1 << 10, 1, 1, 8,
+                                128, 1, s, 256, nullptr),
+         FA_ERR_WORKSPACE);
+
   // ---- fa_fwd_varlen ----
   EXPECT(fa_fwd_varlen(A, A, A, A, Af, Ai, nullptr, 2, 4, 2, 100, 100, 64,
                        128, 1, -1, -1, s, nullptr),

@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
     for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_fwd_splitkv",
               "fa_fwd_varlen", "fa_fwd_masked",
               "fa_splitkv_num_splits", "fa_fp8_quantize",
+              "fa_fwd_splitkv_noalloc",
               "fa_status_string",
               "fa_last_hip_error", "fa_version"):
         assert n in names
@@ -113,6 +114,30 @@ def test_misaligned(lib, which):
 def test_invalid_before_unsupported_before_misaligned(lib):
     assert _fwd(lib, q=M, d=96, N=0) == fa.FA_ERR_INVALID_ARGUMENT
     assert _fwd(lib, q=M, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_splitkv_validation(lib):
+    """The entry point without a workspace checks its arguments like
+    fa_fwd_splitkv, then whether the sizes fit its fixed scratch (4 Mi
+    floats), before touching the GPU."""
+    f = lib.fa_fwd_splitkv_noalloc
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    ok = (1, 8, 2, 1, 4096, 128, 1, 0.1, 8)
+    assert f(None, A, A, A, A, *ok, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert f(A, A, A, A, A, 1, 8, 2, 1, 4096, 128, 1, 0.1, 0,
+             None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert f(A, A, A, A, A, 1, 8, 2, 1, 4096, 64, 1, 0.1, 8,
+             None) == fa.FA_ERR_UNSUPPORTED
+    assert f(M, A, A, A, A, *ok, None) == fa.FA_ERR_MISALIGNED
+    # 256 splits x 16384 rows x 129 floats > 4 Mi floats
+    assert f(A, A, A, A, A, 2, 16, 4, 512, 4096, 128, 1, 0.1, 256,
+             None) == fa.FA_ERR_WORKSPACE
+    # the scratch check comes last: a misaligned pointer is reported first
+    assert f(M, A, A, A, A, 2, 16, 4, 512, 4096, 128, 1, 0.1, 256,
+             None) == fa.FA_ERR_MISALIGNED
+    assert b"scratch" in lib.fa_status_string(fa.FA_ERR_WORKSPACE)
 
 
 def test_quantize_validation(lib):
