@@ -202,7 +202,7 @@ def _rates(iters: int) -> dict:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built")
     lib = ctypes.CDLL(path)
-    lib.fa_probe_rates.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2
+    lib.fa_probe_rates.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 3
     lib.fa_probe_rates.restype = ctypes.c_int
     torch.cuda.set_device(0)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -215,7 +215,7 @@ def _rates(iters: int) -> dict:
         runs = []
         for rep in range(4):              # the first run warms the clock
             rc = lib.fa_probe_rates(ia, ib, waves, na, iters, cus,
-                                    out.data_ptr(), stream)
+                                    out.data_ptr(), None, stream)
             if rc != 0:
                 raise RuntimeError(f"fa_probe_rates({a}, {b}) = {rc}")
             torch.cuda.synchronize()
@@ -268,7 +268,113 @@ def _rates(iters: int) -> dict:
         _progress(json.dumps(row))
     return {"iters": iters, "cus": cus, "bodies": {k: v[2] for k, v in
                                                    PROBE_BODIES.items()},
-            "rows": rows}
+            "rows": rows, "mfma_ceiling": _mfma_ceiling(lib)}
+
+
+def _amd_smi_sample():
+    """(mean GFX clock over the XCDs in MHz, socket power in W) from one
+    amd-smi call, or None."""
+    import shutil
+    import subprocess
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    try:
+        r = subprocess.run([smi, "metric", "-g", "0", "--clock", "--power",
+                            "--json"], capture_output=True, text=True,
+                           timeout=10)
+        g = json.loads(r.stdout)["gpu_data"][0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        pw = g["power"]["socket_power"]["value"]
+        return sum(clks) / len(clks), float(pw)
+    except Exception:                     # tool missing or output changed
+        return None
+
+
+def _under_load(fn, seconds: float):
+    """Calls fn() back to back for `seconds` while a thread samples the GPU
+    clock and socket power with amd-smi (a subprocess); returns the medians
+    over the samples after the first third of the span (the clock settles
+    after the first tens of ms), or None if no sample came back."""
+    import statistics
+    import threading
+    import torch
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            v = _amd_smi_sample()
+            if v is not None and time.perf_counter() - t0 > seconds / 3:
+                samples.append(v)
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()       # bound the queue
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"gfx_mhz": round(statistics.median(c for c, _ in samples), 1),
+            "socket_w": round(statistics.median(p for _, p in samples), 1),
+            "samples": len(samples), "launches": n,
+            "how": "amd-smi metric --clock --power from a subprocess, median "
+                   "of the samples taken while the same launches ran back "
+                   "to back (after the first third of the span)"}
+
+
+def _mfma_ceiling(lib) -> dict:
+    """The matrix rate this card sustains under its power limit on operands
+    like the attention's: every SIMD runs two waves of back-to-back MFMAs
+    whose operands (2 A and 2 B fragments, paired in turn) hold N(0,1)
+    values, for ~0.3 s.  TFLOP/s from HIP events; the shader clock from the
+    probe's own s_memtime / s_memrealtime and from amd-smi."""
+    import statistics
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    res = {}
+    for name, body, flop, iters, make in (
+            ("bf16_32x32x16", 12, 32 * 32 * 16 * 2, 100000,
+             lambda: torch.randn(512 * 16, device="cuda:0", generator=g)
+             .to(torch.bfloat16)),
+            ("fp8_32x32x64", 13, 32 * 32 * 64 * 2, 50000,
+             lambda: torch.randn(512 * 32, device="cuda:0", generator=g)
+             .to(torch.float8_e4m3fn))):
+        data = make().view(torch.uint8).contiguous()
+        assert data.numel() == 512 * 32 and data.data_ptr() % 32 == 0
+        waves = 8
+        out = torch.zeros(cus * waves * 3, dtype=torch.int64, device="cuda:0")
+
+        def launch():
+            rc = lib.fa_probe_rates(body, 0, waves, 2, iters, cus,
+                                    out.data_ptr(), data.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"fa_probe_rates({body}) = {rc}")
+
+        for _ in range(2):
+            launch()
+        load = _under_load(launch, 0.3)
+        tm = _time_launches(launch, 8, 2)
+        t = cus * waves * iters * 4 * flop / (tm["mean"] * 1e-3) / 1e12
+        o = out.view(cus, waves, 3).cpu().double()
+        ghz = float((o[:, :, 0] / o[:, :, 1]).median()) * 0.1
+        peak = BF16_PEAK_TFLOPS if body == 12 else FP8_PEAK_TFLOPS
+        res[name] = {"TFLOP/s": round(t, 1), "frac_of_peak": round(t / peak, 4),
+                     "shader_ghz": round(ghz, 3),
+                     "frac_of_peak_at_that_clock": round(t / (peak * ghz / 2.4), 4),
+                     "under_load": load}
+        _progress(f"mfma ceiling {name}: {res[name]}")
+    return res
 
 
 def main() -> int:
@@ -329,6 +435,13 @@ def main() -> int:
     ms = head["mean"]
     tflops = w.flops / (ms * 1e-3) / 1e12
     _progress(f"{w.name}: {ms:.4f} ms, {tflops:.1f} TFLOP/s")
+    # The clock the card runs this kernel at (power-limited): amd-smi samples
+    # while the same launches run back to back for a second.
+    clock = _under_load(step, 1.0)
+    if clock is not None:
+        clock["frac_of_peak_at_that_clock"] = round(
+            tflops / (BF16_PEAK_TFLOPS * clock["gfx_mhz"] / 2400.0), 4)
+    _progress(f"clock under load: {clock}")
 
     extras = {}
     if not args.no_extras:
@@ -477,6 +590,17 @@ def main() -> int:
             "frac_of_hbm_peak": round(nbytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         _progress(f"fp8_quantize_hadamard_per_tensor: {extras['fp8_quantize_hadamard_per_tensor']}")
         del xq, xk, xv, q8, k8, v8, oo, ll
+        # Context, not part of the path: the matrix rate the card sustains
+        # under its power limit on N(0,1) operands (MFMAs only, no softmax,
+        # no memory traffic).
+        probe = os.path.join(os.path.dirname(fa.__file__), "libfa_probe.so")
+        if os.path.exists(probe):
+            import ctypes
+            plib = ctypes.CDLL(probe)
+            plib.fa_probe_rates.argtypes = [ctypes.c_int] * 6 + \
+                [ctypes.c_void_p] * 3
+            plib.fa_probe_rates.restype = ctypes.c_int
+            extras["mfma_only_randn_ceiling"] = _mfma_ceiling(plib)
         # Context, not part of the path: the vendor bf16 GEMM (hipBLASLt via
         # torch.matmul) on N(0,1) operands of the same distribution, i.e. what
         # a tuned library contraction reaches on this card under its power
@@ -516,6 +640,7 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv,
                    "N": w.N, "d": w.d, "causal": w.causal},
         "frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "clock_under_load": clock,
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),

@@ -44,6 +44,12 @@ enum Body {
   B_MFMA8_EXP = 9,    // 1 f8 MFMA + 8 exp + 8 fma (one softmax slot)
   B_MFMA16_EXP = 10,  // 1 bf16 MFMA + 4 exp + 4 fma
   B_EXP_CHAIN = 11,   // 4 x (v_fma_f32 -> v_exp_f32 -> v_add_f32), + 4 adds
+  // MFMAs on operands from the caller's data (random values): 2 A and 2 B
+  // fragments paired so that an operand changes from one MFMA to the next
+  // as in a real product (switching activity sets the power drawn), few
+  // enough to stay in registers beside the 4 accumulators.
+  B_MFMA16_DATA = 12,  // 4 x v_mfma_f32_32x32x16_bf16
+  B_MFMA8_DATA = 13,   // 4 x v_mfma_scale_f32_32x32x64_f8f6f4
 };
 
 struct Regs {
@@ -51,6 +57,7 @@ struct Regs {
   float y, z;
   int w[8];
   f32x16_t acc[4];
+  i32x8_t da[2], db[2];     // data operands (B_MFMA*_DATA)
 };
 
 __device__ __forceinline__ void fma16(Regs& r, int first, int n) {
@@ -131,6 +138,30 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
       exp16(r, 4 * j, 2);
       fma16(r, 4 * j + 2, 2);
     }
+  } else if constexpr (BODY == B_MFMA16_DATA) {
+    // Fragment j: A from half j/2 of da[j%2], B from half j%2 of db[j/2].
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x8_t ra = r.da[j & 1], rb = r.db[j >> 1];
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, (j >> 1) ? __builtin_shufflevector(ra, ra, 4, 5, 6, 7)
+                             : __builtin_shufflevector(ra, ra, 0, 1, 2, 3));
+      const bf16x8_t b = __builtin_bit_cast(
+          bf16x8_t, (j & 1) ? __builtin_shufflevector(rb, rb, 4, 5, 6, 7)
+                            : __builtin_shufflevector(rb, rb, 0, 1, 2, 3));
+      r.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, r.acc[j], 0, 0,
+                                                         0);
+      asm volatile("" : "+v"(r.acc[j]));
+    }
+  } else if constexpr (BODY == B_MFMA8_DATA) {
+    // Operand pairs (da[0], db[0]), (da[1], db[0]), (da[0], db[1]),
+    // (da[1], db[1]): one operand changes from each MFMA to the next.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          r.da[j & 1], r.db[j >> 1], r.acc[j], 0, 0, 0, 127, 0, 127);
+      asm volatile("" : "+v"(r.acc[j]));
+    }
   } else if constexpr (BODY == B_EXP_CHAIN) {
     // The softmax's dependent sequence: scale and shift, exponential, sum.
     // Written with builtins so that the compiler inserts the wait states a
@@ -154,6 +185,7 @@ __device__ __forceinline__ void run(Regs& r, int iters, const i32x8_t& a8,
 
 template <int A, int B>
 __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
+                                                     const i32x8_t* data,
                                                      int iters, int na,
                                                      float seed) {
   __shared__ float reserve[24576];      // 96 KiB: one workgroup per CU
@@ -169,6 +201,13 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   for (int i = 0; i < 8; ++i) r.w[i] = i;
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
+  // Data operands: lane-dependent fragments of the caller's 512-entry
+  // buffer (all zeros when no buffer is given).
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    r.da[j] = data ? data[(lane + 64 * j) & 511] : i32x8_t{};
+    r.db[j] = data ? data[(lane + 64 * j + 256) & 511] : i32x8_t{};
+  }
   const int s8 = 0x38383838 + (lane & 1);   // e4m3 codes near 1.0
   const i32x8_t a8 = {s8, s8, s8, s8, s8, s8, s8, s8};
   bf16x8_t a16;
@@ -194,6 +233,9 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.w[i]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) sink += r.acc[j][lane & 15];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    sink += static_cast<float>(r.da[j][lane & 7] ^ r.db[j][lane & 7]);
   if (iters < 0) {
     reserve[tid] = sink;
     __syncthreads();
@@ -209,15 +251,15 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
 }
 
 template <int A, int B>
-hipError_t launch(unsigned long long* out, int iters, int na, int waves,
-                  int grid, hipStream_t s) {
+hipError_t launch(unsigned long long* out, const i32x8_t* data, int iters,
+                  int na, int waves, int grid, hipStream_t s) {
   hipLaunchKernelGGL((probe_kernel<A, B>), dim3(grid), dim3(64 * waves), 0, s,
-                     out, iters, na, 1.0e-3f);
+                     out, data, iters, na, 1.0e-3f);
   return hipGetLastError();
 }
 
-typedef hipError_t (*launch_fn)(unsigned long long*, int, int, int, int,
-                                hipStream_t);
+typedef hipError_t (*launch_fn)(unsigned long long*, const i32x8_t*, int, int,
+                                int, int, hipStream_t);
 
 template <int A>
 launch_fn pick_b(int b) {
@@ -238,6 +280,15 @@ launch_fn pick_b(int b) {
   }
 }
 
+// Bodies that run alone (B idle): the data-operand MFMAs.
+launch_fn pick_alone(int a) {
+  switch (a) {
+    case B_MFMA16_DATA: return launch<B_MFMA16_DATA, B_IDLE>;
+    case B_MFMA8_DATA: return launch<B_MFMA8_DATA, B_IDLE>;
+    default: return nullptr;
+  }
+}
+
 launch_fn pick(int a, int b) {
   switch (a) {
     case B_FMA: return pick_b<B_FMA>(b);
@@ -251,6 +302,8 @@ launch_fn pick(int a, int b) {
     case B_MFMA8_EXP: return pick_b<B_MFMA8_EXP>(b);
     case B_MFMA16_EXP: return pick_b<B_MFMA16_EXP>(b);
     case B_EXP_CHAIN: return pick_b<B_EXP_CHAIN>(b);
+    case B_MFMA16_DATA:
+    case B_MFMA8_DATA: return b == B_IDLE ? pick_alone(a) : nullptr;
     default: return nullptr;
   }
 }
@@ -260,13 +313,17 @@ launch_fn pick(int a, int b) {
 // Contract in include/fa_probe.h.
 extern "C" __attribute__((visibility("default"))) int fa_probe_rates(
     int a, int b, int waves, int na, int iters, int grid,
-    unsigned long long* out, void* stream) {
+    unsigned long long* out, const void* data, void* stream) {
   if (!out || waves < 4 || waves > 16 || waves % 4 != 0 || na < 0 ||
       na > waves / 4 || iters < 1 || grid < 1)
     return 1;
+  if ((a == B_MFMA16_DATA || a == B_MFMA8_DATA) &&
+      (!data || (reinterpret_cast<uintptr_t>(data) & 31u)))
+    return 1;
   const launch_fn f = pick(a, b);
   if (!f) return 1;
-  return f(out, iters, na, waves, grid, static_cast<hipStream_t>(stream)) ==
+  return f(out, static_cast<const i32x8_t*>(data), iters, na, waves, grid,
+           static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? 0
              : 4;

@@ -24,7 +24,9 @@ extern "C" {
  *           2 v_exp_f32, 3 exp + fma interleaved, 4 v_cvt_pk_fp8_f32,
  *           5 v_maximum3_f32, 6 v_add_f32, 7 f8 MFMA 32x32x64, 8 bf16 MFMA
  *           32x32x16, 9 f8 MFMA with exp / fma, 10 bf16 MFMA with exp and
- *           fma, 11 fma -> exp -> add chains; b may also be 0, idle).
+ *           fma, 11 fma -> exp -> add chains, 12 bf16 MFMA and 13 f8 MFMA
+ *           on operands from `data`, 2 A and 2 B fragments paired in turn; b may also be 0,
+ *           idle, and must be for bodies 12 and 13).
  *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
  *           CU, so waves / 4 waves on each SIMD).
  *   na      the first 4 * na waves run body a, the others body b.
@@ -34,12 +36,16 @@ extern "C" {
  *           wave in (workgroup, wave) order, shader-clock cycles between the
  *           two clock reads, 100 MHz reference ticks over the same span, and
  *           the wave's HW_ID register (SIMD in bits 5:4).
+ *   data    device, 512 entries of 32 bytes, 32-byte aligned (read only):
+ *           operand values of bodies 12 and 13 (lane l, fragment j reads
+ *           entries (l + 64 j) % 512 and (l + 64 j + 256) % 512); may be
+ *           NULL for the other bodies.
  *   stream  hipStream_t or NULL; one kernel is enqueued.
  *   Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the
  *   launch failed.
  */
 int fa_probe_rates(int a, int b, int waves, int na, int iters, int grid,
-                   unsigned long long* out, void* stream);
+                   unsigned long long* out, const void* data, void* stream);
 
 #ifdef __cplusplus
 }

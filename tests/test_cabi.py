@@ -55,13 +55,16 @@ def test_probe_library_exports_its_header():
     assert names == ["fa_probe_rates"]
     plib = ctypes.CDLL(build.PROBE_LIB)
     f = plib.fa_probe_rates
-    f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2
+    f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 3
     f.restype = ctypes.c_int
-    assert f(1, 0, 4, 1, 8, 1, None, None) == 1          # null output
-    assert f(1, 0, 6, 1, 8, 1, A, None) == 1             # waves not 4k
-    assert f(1, 0, 4, 2, 8, 1, A, None) == 1             # na > waves / 4
-    assert f(99, 0, 4, 1, 8, 1, A, None) == 1            # unknown body
-    assert f(0, 0, 4, 1, 8, 1, A, None) == 1             # body a idle
+    assert f(1, 0, 4, 1, 8, 1, None, None, None) == 1    # null output
+    assert f(1, 0, 6, 1, 8, 1, A, None, None) == 1       # waves not 4k
+    assert f(1, 0, 4, 2, 8, 1, A, None, None) == 1       # na > waves / 4
+    assert f(99, 0, 4, 1, 8, 1, A, None, None) == 1      # unknown body
+    assert f(0, 0, 4, 1, 8, 1, A, None, None) == 1       # body a idle
+    assert f(12, 0, 4, 1, 8, 1, A, None, None) == 1      # data body, no data
+    assert f(12, 0, 4, 1, 8, 1, A, M, None) == 1         # data misaligned
+    assert f(13, 1, 8, 1, 8, 1, A, A, None) == 1         # data body mixed
 
 
 def test_version_and_status_strings(lib):
