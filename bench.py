@@ -175,18 +175,27 @@ PROBE_BODIES = {
     "mfma_f8+exp": (9, 4, "f8 MFMA, each with 8 exp or 8 fma"),
     "mfma_bf16+exp": (10, 4, "bf16 MFMA, each with 2 exp + 2 fma"),
     "exp_chain": (11, 16, "4 x (fma -> exp -> add) + 4 add"),
+    "dot2_bf16": (14, 16, "v_dot2c_f32_bf16"),
+    "mov_b64": (15, 16, "v_mov_b64"),
+    "cvt_pk_bf16": (16, 16, "v_cvt_pk_bf16_f32"),
+    "mfma_bf16+add": (17, 4, "bf16 MFMA, each with 4 v_add_f32"),
+    "mfma_bf16+dot2": (18, 4, "bf16 MFMA, each with 4 v_dot2c_f32_bf16"),
+    "mfma_bf16+mov64": (19, 4, "bf16 MFMA, each with 4 v_mov_b64"),
 }
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
-# CU, wave w on SIMD w % 4.
+# CU, four waves per SIMD at most (the SIMD of each wave is read from its
+# HW_ID).
 PROBE_CONFIGS = (
     [(b, "idle", 4 * n, n) for n in (1, 2, 4)
      for b in ("fma", "exp", "exp+fma", "add", "cvt_pk_fp8", "maximum3",
-               "exp_chain")]
+               "exp_chain", "dot2_bf16", "mov_b64", "cvt_pk_bf16")]
     + [(b, "idle", 4 * n, n) for n in (1, 2)
-       for b in ("mfma_f8", "mfma_bf16", "mfma_f8+exp", "mfma_bf16+exp")]
+       for b in ("mfma_f8", "mfma_bf16", "mfma_f8+exp", "mfma_bf16+exp",
+                 "mfma_bf16+add", "mfma_bf16+dot2", "mfma_bf16+mov64")]
     + [("mfma_f8", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain")]
-    + [("mfma_bf16", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain")]
+    + [("mfma_bf16", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain",
+                                          "dot2_bf16", "mov_b64")]
     + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
 )
 
@@ -271,15 +280,29 @@ def _rates(iters: int) -> dict:
             "rows": rows, "mfma_ceiling": _mfma_ceiling(lib)}
 
 
+def _under_profiler() -> bool:
+    """rocprofv3 preloads its library into every child process, and there
+    it initialises the GPU, so a child that then replaces itself (a script
+    run through `#!/usr/bin/env`) must not be started at all."""
+    return any(k.startswith("ROCPROF") for k in os.environ) or \
+        "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def _amd_smi_sample():
     """(mean GFX clock over the XCDs in MHz, socket power in W) from one
-    amd-smi call, or None."""
+    amd-smi call, or None.  amd-smi is a Python script: it is run by this
+    interpreter directly, as one child process with no `env` hop."""
     import shutil
     import subprocess
+    if _under_profiler():
+        return None
     smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     try:
-        r = subprocess.run([smi, "metric", "-g", "0", "--clock", "--power",
-                            "--json"], capture_output=True, text=True,
+        with open(smi, "rb") as f:
+            first = f.readline()
+        cmd = [sys.executable, smi] if b"python" in first else [smi]
+        r = subprocess.run(cmd + ["metric", "-g", "0", "--clock", "--power",
+                                  "--json"], capture_output=True, text=True,
                            timeout=10)
         g = json.loads(r.stdout)["gpu_data"][0]
         clks = [v["clk"]["value"] for k, v in g["clock"].items()
@@ -293,8 +316,9 @@ def _amd_smi_sample():
 def _under_load(fn, seconds: float):
     """Calls fn() back to back for `seconds` while a thread samples the GPU
     clock and socket power with amd-smi (a subprocess); returns the medians
-    over the samples after the first third of the span (the clock settles
-    after the first tens of ms), or None if no sample came back."""
+    over the samples taken wholly inside the load (started after its first
+    third, when the clock has settled, and finished before the last launch
+    completed), or None if none was."""
     import statistics
     import threading
     import torch
@@ -302,11 +326,11 @@ def _under_load(fn, seconds: float):
     stop = threading.Event()
 
     def sampler():
-        t0 = time.perf_counter()
         while not stop.is_set():
+            t_a = time.perf_counter()
             v = _amd_smi_sample()
-            if v is not None and time.perf_counter() - t0 > seconds / 3:
-                samples.append(v)
+            if v is not None:
+                samples.append((t_a, time.perf_counter(), v))
             time.sleep(0.02)
 
     th = threading.Thread(target=sampler, daemon=True)
@@ -319,16 +343,18 @@ def _under_load(fn, seconds: float):
         if n % 16 == 0:
             torch.cuda.synchronize()       # bound the queue
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
     stop.set()
     th.join()
-    if not samples:
+    inside = [v for a, b, v in samples if a > t0 + seconds / 3 and b < t1]
+    if not inside:
         return None
-    return {"gfx_mhz": round(statistics.median(c for c, _ in samples), 1),
-            "socket_w": round(statistics.median(p for _, p in samples), 1),
-            "samples": len(samples), "launches": n,
+    return {"gfx_mhz": round(statistics.median(c for c, _ in inside), 1),
+            "socket_w": round(statistics.median(p for _, p in inside), 1),
+            "samples": len(inside), "launches": n,
             "how": "amd-smi metric --clock --power from a subprocess, median "
-                   "of the samples taken while the same launches ran back "
-                   "to back (after the first third of the span)"}
+                   "of the samples taken wholly inside a span of back-to-back "
+                   "launches (after its first third)"}
 
 
 def _mfma_ceiling(lib) -> dict:
@@ -363,7 +389,7 @@ def _mfma_ceiling(lib) -> dict:
 
         for _ in range(2):
             launch()
-        load = _under_load(launch, 0.3)
+        load = _under_load(launch, 1.0)
         tm = _time_launches(launch, 8, 2)
         t = cus * waves * iters * 4 * flop / (tm["mean"] * 1e-3) / 1e12
         o = out.view(cus, waves, 3).cpu().double()

@@ -50,12 +50,21 @@ enum Body {
   // enough to stay in registers beside the 4 accumulators.
   B_MFMA16_DATA = 12,  // 4 x v_mfma_f32_32x32x16_bf16
   B_MFMA8_DATA = 13,   // 4 x v_mfma_scale_f32_32x32x64_f8f6f4
+  // Candidate softmax instructions of the bf16 kernel, alone and beside the
+  // same wave's bf16 MFMAs (4 of them per MFMA).
+  B_DOT2 = 14,         // 16 x v_dot2c_f32_bf16
+  B_MOV64 = 15,        // 16 x v_mov_b64
+  B_CVT16 = 16,        // 16 x v_cvt_pk_bf16_f32
+  B_MFMA16_ADD = 17,   // 4 x (bf16 MFMA + 4 v_add_f32)
+  B_MFMA16_DOT2 = 18,  // 4 x (bf16 MFMA + 4 v_dot2c_f32_bf16)
+  B_MFMA16_MOV64 = 19, // 4 x (bf16 MFMA + 4 v_mov_b64)
 };
 
 struct Regs {
   float x[16];
   float y, z;
   int w[8];
+  double dd[8], dsrc;       // 64-bit move targets and source (B_*MOV64)
   f32x16_t acc[4];
   i32x8_t da[2], db[2];     // data operands (B_MFMA*_DATA)
 };
@@ -70,6 +79,15 @@ __device__ __forceinline__ void exp16(Regs& r, int first, int n) {
 #pragma unroll
   for (int i = first; i < first + n; ++i)
     asm volatile("v_exp_f32 %0, %0" : "+v"(r.x[i]));
+}
+
+__device__ __forceinline__ void dot2(Regs& r, int i) {
+  asm volatile("v_dot2c_f32_bf16 %0, %1, %2"
+               : "+v"(r.x[i]) : "v"(r.w[i & 7]), "v"(r.w[(i + 3) & 7]));
+}
+
+__device__ __forceinline__ void mov64(Regs& r, int i) {
+  asm volatile("v_mov_b64 %0, %1" : "=v"(r.dd[i & 7]) : "v"(r.dsrc));
 }
 
 template <int BODY>
@@ -162,6 +180,34 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
           r.da[j & 1], r.db[j >> 1], r.acc[j], 0, 0, 0, 127, 0, 127);
       asm volatile("" : "+v"(r.acc[j]));
     }
+  } else if constexpr (BODY == B_DOT2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dot2(r, i);
+  } else if constexpr (BODY == B_MOV64) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mov64(r, i);
+  } else if constexpr (BODY == B_CVT16) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2"
+                   : "=v"(r.w[i & 7]) : "v"(r.x[i]), "v"(r.x[(i + 1) & 15]));
+  } else if constexpr (BODY == B_MFMA16_ADD || BODY == B_MFMA16_DOT2 ||
+                       BODY == B_MFMA16_MOV64) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a16, a16, r.acc[j],
+                                                         0, 0, 0);
+      asm volatile("" : "+v"(r.acc[j]));
+#pragma unroll
+      for (int i = 4 * j; i < 4 * j + 4; ++i) {
+        if constexpr (BODY == B_MFMA16_ADD)
+          asm volatile("v_add_f32 %0, %0, %1" : "+v"(r.x[i]) : "v"(r.y));
+        else if constexpr (BODY == B_MFMA16_DOT2)
+          dot2(r, i);
+        else
+          mov64(r, i);
+      }
+    }
   } else if constexpr (BODY == B_EXP_CHAIN) {
     // The softmax's dependent sequence: scale and shift, exponential, sum.
     // Written with builtins so that the compiler inserts the wait states a
@@ -198,7 +244,10 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   r.y = 0.999f;
   r.z = seed;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.w[i] = i;
+  for (int i = 0; i < 8; ++i) r.w[i] = 0x3F803F80 + i;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.dd[i] = seed * i;
+  r.dsrc = seed;
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
   // Data operands: lane-dependent fragments of the caller's 512-entry
@@ -231,6 +280,8 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   for (int i = 0; i < 16; ++i) sink += r.x[i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.w[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.dd[i]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) sink += r.acc[j][lane & 15];
 #pragma unroll
@@ -276,6 +327,9 @@ launch_fn pick_b(int b) {
     case B_MFMA8_EXP: return launch<A, B_MFMA8_EXP>;
     case B_MFMA16_EXP: return launch<A, B_MFMA16_EXP>;
     case B_EXP_CHAIN: return launch<A, B_EXP_CHAIN>;
+    case B_DOT2: return launch<A, B_DOT2>;
+    case B_MOV64: return launch<A, B_MOV64>;
+    case B_CVT16: return launch<A, B_CVT16>;
     default: return nullptr;
   }
 }
@@ -285,6 +339,9 @@ launch_fn pick_alone(int a) {
   switch (a) {
     case B_MFMA16_DATA: return launch<B_MFMA16_DATA, B_IDLE>;
     case B_MFMA8_DATA: return launch<B_MFMA8_DATA, B_IDLE>;
+    case B_MFMA16_ADD: return launch<B_MFMA16_ADD, B_IDLE>;
+    case B_MFMA16_DOT2: return launch<B_MFMA16_DOT2, B_IDLE>;
+    case B_MFMA16_MOV64: return launch<B_MFMA16_MOV64, B_IDLE>;
     default: return nullptr;
   }
 }
@@ -302,6 +359,12 @@ launch_fn pick(int a, int b) {
     case B_MFMA8_EXP: return pick_b<B_MFMA8_EXP>(b);
     case B_MFMA16_EXP: return pick_b<B_MFMA16_EXP>(b);
     case B_EXP_CHAIN: return pick_b<B_EXP_CHAIN>(b);
+    case B_DOT2: return pick_b<B_DOT2>(b);
+    case B_MOV64: return pick_b<B_MOV64>(b);
+    case B_CVT16: return pick_b<B_CVT16>(b);
+    case B_MFMA16_ADD: return b == B_IDLE ? pick_alone(a) : nullptr;
+    case B_MFMA16_DOT2: return b == B_IDLE ? pick_alone(a) : nullptr;
+    case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_DATA:
     case B_MFMA8_DATA: return b == B_IDLE ? pick_alone(a) : nullptr;
     default: return nullptr;

@@ -65,6 +65,8 @@ def test_probe_library_exports_its_header():
     assert f(12, 0, 4, 1, 8, 1, A, None, None) == 1      # data body, no data
     assert f(12, 0, 4, 1, 8, 1, A, M, None) == 1         # data misaligned
     assert f(13, 1, 8, 1, 8, 1, A, A, None) == 1         # data body mixed
+    assert f(18, 1, 8, 1, 8, 1, A, None, None) == 1      # same-wave mix mixed
+    assert f(20, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
 
 
 def test_version_and_status_strings(lib):
