@@ -181,6 +181,7 @@ PROBE_BODIES = {
     "mfma_bf16+add": (17, 4, "bf16 MFMA, each with 4 v_add_f32"),
     "mfma_bf16+dot2": (18, 4, "bf16 MFMA, each with 4 v_dot2c_f32_bf16"),
     "mfma_bf16+mov64": (19, 4, "bf16 MFMA, each with 4 v_mov_b64"),
+    "cvt_scalef32_pk_fp8": (20, 16, "v_cvt_scalef32_pk_fp8_f32"),
 }
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
@@ -189,7 +190,8 @@ PROBE_BODIES = {
 PROBE_CONFIGS = (
     [(b, "idle", 4 * n, n) for n in (1, 2, 4)
      for b in ("fma", "exp", "exp+fma", "add", "cvt_pk_fp8", "maximum3",
-               "exp_chain", "dot2_bf16", "mov_b64", "cvt_pk_bf16")]
+               "exp_chain", "dot2_bf16", "mov_b64", "cvt_pk_bf16",
+               "cvt_scalef32_pk_fp8")]
     + [(b, "idle", 4 * n, n) for n in (1, 2)
        for b in ("mfma_f8", "mfma_bf16", "mfma_f8+exp", "mfma_bf16+exp",
                  "mfma_bf16+add", "mfma_bf16+dot2", "mfma_bf16+mov64")]

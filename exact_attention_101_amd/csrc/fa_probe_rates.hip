@@ -58,6 +58,7 @@ enum Body {
   B_MFMA16_ADD = 17,   // 4 x (bf16 MFMA + 4 v_add_f32)
   B_MFMA16_DOT2 = 18,  // 4 x (bf16 MFMA + 4 v_dot2c_f32_bf16)
   B_MFMA16_MOV64 = 19, // 4 x (bf16 MFMA + 4 v_mov_b64)
+  B_CVT8S = 20,        // 16 x v_cvt_scalef32_pk_fp8_f32
 };
 
 struct Regs {
@@ -186,6 +187,22 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
   } else if constexpr (BODY == B_MOV64) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) mov64(r, i);
+  } else if constexpr (BODY == B_CVT8S) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      typedef __attribute__((ext_vector_type(2))) short s2_t;
+      s2_t o = __builtin_bit_cast(s2_t, r.w[i & 7]);
+      if (i & 8)
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, r.x[i],
+                                                    r.x[(i + 1) & 15], r.y,
+                                                    true);
+      else
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, r.x[i],
+                                                    r.x[(i + 1) & 15], r.y,
+                                                    false);
+      r.w[i & 7] = __builtin_bit_cast(int, o);
+      asm volatile("" : "+v"(r.w[i & 7]));
+    }
   } else if constexpr (BODY == B_CVT16) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -330,6 +347,7 @@ launch_fn pick_b(int b) {
     case B_DOT2: return launch<A, B_DOT2>;
     case B_MOV64: return launch<A, B_MOV64>;
     case B_CVT16: return launch<A, B_CVT16>;
+    case B_CVT8S: return launch<A, B_CVT8S>;
     default: return nullptr;
   }
 }
@@ -362,6 +380,7 @@ launch_fn pick(int a, int b) {
     case B_DOT2: return pick_b<B_DOT2>(b);
     case B_MOV64: return pick_b<B_MOV64>(b);
     case B_CVT16: return pick_b<B_CVT16>(b);
+    case B_CVT8S: return pick_b<B_CVT8S>(b);
     case B_MFMA16_ADD: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_DOT2: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;

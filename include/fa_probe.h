@@ -28,8 +28,9 @@ extern "C" {
  *           on operands from `data`, 2 A and 2 B fragments paired in
  *           turn, 14 v_dot2c_f32_bf16, 15 v_mov_b64, 16 v_cvt_pk_bf16_f32,
  *           17 / 18 / 19 bf16 MFMA each followed by 4 v_add_f32 / 4
- *           v_dot2c_f32_bf16 / 4 v_mov_b64 in the same wave; b may also be
- *           0, idle, and must be for bodies 12, 13 and 17 to 19).
+ *           v_dot2c_f32_bf16 / 4 v_mov_b64 in the same wave, 20
+ *           v_cvt_scalef32_pk_fp8_f32; b may also be 0, idle, and must be
+ *           for bodies 12, 13 and 17 to 19).
  *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
  *           CU, so waves / 4 waves on each SIMD).
  *   na      the first 4 * na waves run body a, the others body b.

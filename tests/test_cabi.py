@@ -66,7 +66,7 @@ def test_probe_library_exports_its_header():
     assert f(12, 0, 4, 1, 8, 1, A, M, None) == 1         # data misaligned
     assert f(13, 1, 8, 1, 8, 1, A, A, None) == 1         # data body mixed
     assert f(18, 1, 8, 1, 8, 1, A, None, None) == 1      # same-wave mix mixed
-    assert f(20, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
+    assert f(21, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
 
 
 def test_version_and_status_strings(lib):
@@ -255,3 +255,4 @@ def test_masked_unsupported_and_alignment(lib):
     assert _mk(lib, Nk=262144, q=M) == fa.FA_ERR_MISALIGNED
     assert _mk(lib, mask=A + 2) == fa.FA_ERR_MISALIGNED
     assert _mk(lib, lse=A + 1) == fa.FA_ERR_MISALIGNED
+
