@@ -19,8 +19,7 @@ SERIAL_LIB = os.path.join(HERE, "libfa_serial.so")
 PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
 PROBE_SOURCES = ["fa_probe_rates.hip"]
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_quant.hip",
-           "fa_bwd_bf16.hip", "fa_splitkv_bf16.hip", "fa_varlen_bf16.hip",
-           "fa_masked_bf16.hip"]
+           "fa_bwd_bf16.hip", "fa_splitkv_bf16.hip", "fa_varlen_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Code generation flags shared by the library build and the ISA checks.

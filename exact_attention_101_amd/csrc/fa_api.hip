@@ -18,7 +18,7 @@ hipError_t splitkv_scratch(float** out);
 int splitkv_auto_splits(int B, int H, int Hkv, int Nq, int Nk);
 hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream);
 hipError_t launch_varlen_bf16(VarlenArgs a, hipStream_t stream);
-hipError_t launch_masked_bf16(MaskArgs a, hipStream_t stream);
+hipError_t launch_fwd_masked_bf16(FwdArgs a, hipStream_t stream);
 hipError_t launch_fp8_quantize(const float* x, uint8_t* x8, float* amax_descale,
                                long long rows, uint64_t sign_lo,
                                uint64_t sign_hi, bool rotate,
@@ -330,24 +330,14 @@ FA_EXPORT int fa_fwd_masked(const void* q, const void* k, const void* v,
       (reinterpret_cast<uintptr_t>(lse) & 3u) ||
       (reinterpret_cast<uintptr_t>(mask) & 3u))
     return FA_ERR_MISALIGNED;
-  fa::MaskArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
+  fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Hkv, Nq, scale);
+  a.total_q = Nq;
+  a.total_k = Nk;
   a.mask = mask;
   a.mask_bs = mask_batch_stride;
   a.mask_hs = mask_head_stride;
-  a.B = B;
-  a.H = H;
-  a.Hkv = Hkv;
-  a.group = H / Hkv;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.c = scale * 1.4426950408889634f;
   return hip_status(
-      fa::launch_masked_bf16(a, static_cast<hipStream_t>(stream)));
+      fa::launch_fwd_masked_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_fp8_quantize(const float* x, void* x8, float* amax_descale,

@@ -47,6 +47,12 @@ struct FwdArgs {
   const int* cu_k;
   int total_q, total_k;
   int left, right;
+  // Masked launches only: bit j % 32 of word j / 32 of a row says whether
+  // key j is visible; mw words per row; batch and head strides in words
+  // (0: one mask shared); total_q / total_k are Nq / Nk.
+  const uint32_t* mask;
+  long long mask_bs, mask_hs;
+  int mw;
 };
 
 // Arguments of one backward pass (bf16, d = 128).  ws holds, per query row
@@ -118,24 +124,7 @@ struct VarlenArgs {
   float c;                // scale * log2(e), signed
 };
 
-// Forward under an arbitrary visibility bit mask.
-struct MaskArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  const uint32_t* mask;   // bit j % 32 of word j / 32 of a row: key j visible
-  long long mask_bs;      // words between batches' masks (0: shared)
-  long long mask_hs;      // words between query heads' masks (0: shared)
-  int B, H, Hkv;
-  int group;              // H / Hkv
-  int Nq, Nk;
-  int W;                  // words per mask row, ceil(Nk / 32)
-  int nqb;                // 128-row query blocks
-  float c;                // scale * log2(e), signed
-};
-constexpr int MASK_MAX_NK = 262144;   // keys a mask may cover
+constexpr int MASK_MAX_NK = 262144;   // keys a mask may cover (masked forward)
 // Variable-length windows with left + right below this many keys (both
 // bounded) run on the 128-row kernel, wider ones on the pipelined kernel.
 constexpr int VARLEN_NARROW = 512;

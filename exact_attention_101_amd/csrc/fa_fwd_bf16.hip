@@ -19,7 +19,8 @@
 //     what 32-row waves need, and LDS traffic is what the matrix cores
 //     otherwise wait on and what the power budget goes to.  The variable-
 //     length configuration uses 8 waves of 32 rows, two per SIMD (more
-//     issue slots for the window masks);
+//     issue slots for the window masks), the masked one 4 waves of 32 rows
+//     (128 rows; two workgroups per CU);
 //   * K and V blocks of BT = 64 keys go from HBM/L2 straight into LDS with
 //     buffer_load_dwordx4 ... lds (no register staging), into two K and two
 //     V stage arrays (distinct arrays, so the compiler can tell the
@@ -64,26 +65,34 @@
 //     from lo's tile), window masks in the masked blocks, and the XCDs fed
 //     by KV head rather than by sequence.  A row that has seen no key keeps
 //     m = -inf and forms P against 0; the first block in which it sees a
-//     key takes the exact step.
+//     key takes the exact step;
+//   * MK (arbitrary visibility masks, same section): before its loop each
+//     workgroup ORs (and ANDs) its rows' mask words into a list of the
+//     64-key tiles some row sees, each flagged if every row sees all of it;
+//     the copies follow the list, so work scales with the visible tiles.
+//     Each lane's mask words of a listed tile are fetched with the tile's K
+//     copy unless the tile is whole for the workgroup, and a block is
+//     masked score by score only where some row of the wave misses a key.
 #include "fa_common.h"
 
 namespace fa {
 
 namespace {
 
-constexpr int BR = 256;                 // query rows per workgroup
 constexpr int BT = 64;                  // keys per K / V stage (copy tile)
 constexpr int BC = 32;                  // keys per compute step
 constexpr float TAU_EXP2 = 256.0f;      // 2^TAU, TAU = 8 (log2 units)
 
-// Waves of a workgroup: NQB 32-row query blocks per wave, NWAVE = 8 / NQB
-// waves (NQB = 2: one wave per SIMD; NQB = 1: two waves per SIMD).
-template <int NQB>
+// Waves of a workgroup: NQB 32-row query blocks per wave and NW waves,
+// BR = 32 NQB NW query rows (NQB = 2, NW = 4: 256 rows, one wave per SIMD;
+// NQB = 1, NW = 8: 256 rows, two waves per SIMD; NQB = 2, NW = 2: 128 rows,
+// two workgroups per CU).
+template <int NQB, int NW = 8 / NQB>
 struct Waves {
-  static constexpr int NWAVE = 8 / NQB;
+  static constexpr int NWAVE = NW;
   static constexpr int QPW = 32 * NQB;            // query rows per wave
   static constexpr int NTHR = 64 * NWAVE;
-  static_assert(NWAVE * QPW == BR, "workgroup rows");
+  static constexpr int BR = NWAVE * QPW;          // query rows per workgroup
 };
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -204,16 +213,30 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
       soffset, 0, 0);
 }
 
-template <int D, bool CAUSAL, int NQB, bool VL = false>
-__global__ void __launch_bounds__(Waves<NQB>::NTHR, 1)
+template <int D, bool CAUSAL, int NQB, bool VL = false, bool MK = false,
+          int NW = 8 / NQB>
+__global__ void __launch_bounds__((Waves<NQB, NW>::NTHR), 1)
 fwd_bf16_kernel(const FwdArgs a) {
-  constexpr int NWAVE = Waves<NQB>::NWAVE;
-  constexpr int QPW = Waves<NQB>::QPW;
+  constexpr int NWAVE = Waves<NQB, NW>::NWAVE;
+  constexpr int QPW = Waves<NQB, NW>::QPW;
+  constexpr int BR = Waves<NQB, NW>::BR;
+  // Rows may see no key of a block, or none at all (windows, masks).
+  constexpr bool VM = VL || MK;
   using G = Geo<D, NWAVE>;
   __shared__ uint4 Ks0[G::KSLOTS];
   __shared__ uint4 Ks1[G::KSLOTS];
   __shared__ uint4 Vs0[G::VSLOTS];
   __shared__ uint4 Vs1[G::VSLOTS];
+  // MK: the key tiles some row of the workgroup sees, in order (tl: tile
+  // index, bit 15 set if every row sees all of the tile's keys below NK),
+  // their count (tl_n), and while they are gathered a bit per tile that
+  // some row sees (tfl) and one per tile that some row does not see whole
+  // (tfp).
+  constexpr int NTL = MK ? MASK_MAX_NK / BT : 1;
+  __shared__ uint16_t tl[NTL];
+  __shared__ uint32_t tfl[MK ? NTL / 32 : 1];
+  __shared__ uint32_t tfp[MK ? NTL / 32 : 1];
+  __shared__ int tl_n[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,6 +302,11 @@ fwd_bf16_kernel(const FwdArgs a) {
     wr = a.right;
     qrow0 = static_cast<int64_t>(hq) * a.total_q + q_beg;
     krow0 = static_cast<int64_t>(hk) * a.total_k + k_beg;
+  } else if constexpr (MK) {
+    NQ = a.total_q;
+    NK = a.total_k;
+    qrow0 = (static_cast<int64_t>(b) * a.H + hq) * NQ;
+    krow0 = (static_cast<int64_t>(b) * a.Hkv + hk) * NK;
   } else {
     NQ = NK = a.N;
     qrow0 = (static_cast<int64_t>(b) * a.H + hq) * a.N;
@@ -326,6 +354,166 @@ fwd_bf16_kernel(const FwdArgs a) {
     }
   }
 
+  // ---- MK: the 64-key tiles some row of the workgroup sees ----
+  // Each wave ORs the mask rows q0 + wave, q0 + wave + NWAVE, ... word by
+  // word (lane L holds words 4 L .. 4 L + 3 of each 256-word chunk, four
+  // rows in flight), marks the tiles with a visible key in tfl, and wave 0
+  // turns the marks into the ordered list tl.  Bits past NK are ignored.
+  int ntl = 0;
+  const uint32_t* mrow[NQB];              // this lane's mask rows
+  if constexpr (MK) {
+    const uint32_t* mp = a.mask + b * a.mask_bs + hq * a.mask_hs;
+    const int W = a.mw;
+    const int nt = (NK + BT - 1) / BT;
+    const int ntw = (nt + 31) / 32;
+    const int r1 = min(NQ, q0 + BR);
+    for (int i = tid; i < ntw; i += Waves<NQB, NW>::NTHR) {
+      tfl[i] = 0u;
+      tfp[i] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < NQB; ++j)
+      mrow[j] = mp + static_cast<int64_t>(min(qw0 + 32 * j + li, NQ - 1)) * W;
+    __syncthreads();
+    const uint32_t tail = (NK & 31) ? (1u << (NK & 31)) - 1u : ~0u;
+    // Rows of 16-byte aligned words (W % 4 == 0 and an aligned mask) are
+    // read 16 bytes per lane, sixteen rows in flight; others word by word.
+    const bool vec = (W & 3) == 0 &&
+                     (reinterpret_cast<uintptr_t>(mp) & 15) == 0;
+    for (int c0 = 0; c0 < W; c0 += 256) {
+      const int j0 = c0 + 4 * lane;
+      uint32_t acc[4] = {0u, 0u, 0u, 0u};       // OR over the rows
+      uint32_t all[4] = {~0u, ~0u, ~0u, ~0u};   // AND over the rows
+      if (vec) {
+        for (int r = q0 + wave; r < r1; r += 16 * NWAVE) {
+          uint4 x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int rr = r + u * NWAVE;
+            const uint32_t* rp =
+                mp + static_cast<int64_t>(rr < r1 ? rr : r) * W;
+            x[u] = (j0 < W) ? *reinterpret_cast<const uint4*>(rp + j0)
+                            : make_uint4(0u, 0u, 0u, 0u);
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            acc[0] |= x[u].x;
+            acc[1] |= x[u].y;
+            acc[2] |= x[u].z;
+            acc[3] |= x[u].w;
+            all[0] &= x[u].x;
+            all[1] &= x[u].y;
+            all[2] &= x[u].z;
+            all[3] &= x[u].w;
+          }
+        }
+      } else {
+        for (int r = q0 + wave; r < r1; r += 4 * NWAVE) {
+          uint32_t x[4][4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int rr = r + u * NWAVE;
+            const uint32_t* rp =
+                mp + static_cast<int64_t>(rr < r1 ? rr : r) * W;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              x[u][k] = (j0 + k < W) ? rp[j0 + k] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              acc[k] |= x[u][k];
+              all[k] &= x[u][k];
+            }
+        }
+      }
+      // Bits past NK are ignored: never seen, never missing.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (j0 + k == W - 1) {
+          acc[k] &= tail;
+          all[k] |= ~tail;
+        }
+      }
+      // Words 4 L .. 4 L + 3 are tiles 2 L' and 2 L' + 1 (L' = j0 / 4).
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int t = j0 / 2 + e;
+        if (t < nt) {
+          if ((acc[2 * e] | acc[2 * e + 1]) != 0u)
+            atomicOr(&tfl[t >> 5], 1u << (t & 31));
+          if ((all[2 * e] & all[2 * e + 1]) != ~0u)
+            atomicOr(&tfp[t >> 5], 1u << (t & 31));
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // Lane L gathers words 2 L and 2 L + 1 of tfl (up to 4096 tiles).
+      const uint32_t f0 = (2 * lane < ntw) ? tfl[2 * lane] : 0u;
+      const uint32_t f1 = (2 * lane + 1 < ntw) ? tfl[2 * lane + 1] : 0u;
+      const uint32_t p0 = (2 * lane < ntw) ? tfp[2 * lane] : ~0u;
+      const uint32_t p1 = (2 * lane + 1 < ntw) ? tfp[2 * lane + 1] : ~0u;
+      const int cnt = __builtin_popcount(f0) + __builtin_popcount(f1);
+      int incl = cnt;
+#pragma unroll
+      for (int dlt = 1; dlt < 64; dlt <<= 1) {
+        const int y = __shfl_up(incl, dlt);
+        if (lane >= dlt) incl += y;
+      }
+      int pos = incl - cnt;
+      for (uint32_t f = f0; f; f &= f - 1u) {
+        const int b = __builtin_ctz(f);
+        tl[pos++] = static_cast<uint16_t>(64 * lane + b +
+                                          (((p0 >> b) & 1u) ? 0 : 0x8000));
+      }
+      for (uint32_t f = f1; f; f &= f - 1u) {
+        const int b = __builtin_ctz(f);
+        tl[pos++] = static_cast<uint16_t>(64 * lane + 32 + b +
+                                          (((p1 >> b) & 1u) ? 0 : 0x8000));
+      }
+      if (lane == 63) tl_n[0] = incl;
+    }
+    __syncthreads();
+    ntl = __builtin_amdgcn_readfirstlane(tl_n[0]);
+  }
+  // MK: the list is read through two 64-entry windows in registers (lane L
+  // holds entries 64 w0 + L and 64 (w0 + 1) + L), so that a tile's entry
+  // comes from v_readlane and not from an LDS read the wave must wait for;
+  // positions are asked for in increasing order, so the windows move on
+  // once every 64 tiles.
+  int win0 = 0, win1 = 0, w0 = 0;
+  if constexpr (MK) {
+    win0 = tl[lane];
+    win1 = tl[64 + lane];
+  }
+  // Entry of tile position t < ntl (MK).
+  auto entry = [&](int t) -> int {
+    while ((t >> 6) >= w0 + 2) {              // rare: next window
+      win0 = win1;
+      const int i = 64 * (w0 + 2) + lane;
+      win1 = i < NTL ? tl[i] : 0;
+      ++w0;
+    }
+    return __builtin_amdgcn_readlane((t >> 6) == w0 ? win0 : win1, t & 63);
+  };
+  // First key of tile position t (MK: of the t-th listed tile; positions
+  // past the list are virtual, their copies read nothing), and (MK) whether
+  // every row of the workgroup sees all of its keys below NK.
+  auto tkv = [&](int t) {
+    if constexpr (MK)
+      return t < ntl ? (entry(t) & 0x7FFF) * BT : NK;
+    else
+      return t * BT;
+  };
+  auto tfull = [&](int t) {
+    if constexpr (MK)
+      return t >= ntl || (entry(t) & 0x8000) != 0;
+    else
+      return true;
+  };
+
   // ---- per-lane byte offsets of this wave's tile copies ----
   // K copy j (j = wave + 4 i) fills slots 64 j .. 64 j + 63: lane L writes
   // slot 64 j + L = row * KSL + chunk; pad slots re-read the last chunk.
@@ -338,7 +526,10 @@ fwd_bf16_kernel(const FwdArgs a) {
     const int ch = min(slot - row * G::KSL, G::NCH - 1);
     return static_cast<uint32_t>((row * D + ch * 8) * 2);
   };
-  constexpr int KREG = G::KPW < 4 ? G::KPW : 4;   // copies with a register
+  // Copies with a precomputed offset (four, or eight with two waves, which
+  // issue twice the copies each).
+  constexpr int KRMAX = NWAVE == 2 ? 8 : 4;
+  constexpr int KREG = G::KPW < KRMAX ? G::KPW : KRMAX;
   constexpr int KPK = (KREG + 1) / 2;
   uint32_t koff2[KPK];
 #pragma unroll
@@ -369,7 +560,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     return i < G::KINS / NWAVE || i < kinst;
   };
 
-  const int ntiles = (kv_end + BT - 1) / BT;
+  const int ntiles = MK ? ntl : (kv_end + BT - 1) / BT;
   const int nblk = 2 * ntiles;          // key blocks of BC keys
   // Steps 1 .. nsteps run in rounds of four; step b ends with O += P(b-1)
   // V(b-1), so the last real block is done at step nblk.  Blocks past the
@@ -386,7 +577,7 @@ fwd_bf16_kernel(const FwdArgs a) {
         rows * D * 2, 0x00020000);
   };
   auto copy_k = [&](int tile, const uint4* stage) {
-    const auto rs = rsrc_at(kp, tile * BT);
+    const auto rs = rsrc_at(kp, tkv(tile));
 #pragma unroll
     for (int i = 0; i < G::KPW; ++i)
       if (has_k_copy(i))
@@ -395,7 +586,7 @@ fwd_bf16_kernel(const FwdArgs a) {
                              : k_offset(i));
   };
   auto copy_v = [&](int tile, const uint4* stage) {
-    const auto rs = rsrc_at(vp, tile * BT);
+    const auto rs = rsrc_at(vp, tkv(tile));
 #pragma unroll
     for (int i = 0; i < G::VPW; ++i)
       copy_to_lds(rs, stage + 64 * (wave + NWAVE * i), voff0, VSTRIDE * i);
@@ -456,11 +647,23 @@ fwd_bf16_kernel(const FwdArgs a) {
   // VL: vis[j] says whether the row of query block j sees any key of the
   // block (rows that have seen none so far must take the exact step on the
   // first block where they do).
+  // MK: mwv[j] holds the mask word of the block for this lane's row of
+  // query block j (bits past NK cleared).
+  uint32_t mwv[NQB];
   auto apply_mask = [&](f32x16_t (&s)[NQB], int kv0, bool (&vis)[NQB]) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       const int qrow = qw0 + 32 * j + li;
-      if constexpr (VL) {
+      if constexpr (MK) {
+        // Lane half h holds keys 8 h + kx, kx = 16 (r / 8) + r % 8.
+        const uint32_t mb = mwv[j] >> (8 * h);
+        vis[j] = (mb & 0x00FF00FFu) != 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kx = 16 * (r >> 3) + (r & 7);
+          if (!((mb >> kx) & 1u)) s[j][r] = -__builtin_inff();
+        }
+      } else if constexpr (VL) {
         // This row's visible keys [jlo, jhi], relative to the lane's first
         // key of the block: score r (key base + kx) is kept iff
         // rlo <= kx <= rhi.
@@ -512,6 +715,51 @@ fwd_bf16_kernel(const FwdArgs a) {
              (wl >= 0 && kv0 < qw0 + QPW - 1 + off - wl);
     else
       return (kv0 + BC > NK) || (CAUSAL && kv0 + BC - 1 > qw0);
+  };
+  // MK: the mask words of block blk (tile position blk / 2, half blk % 2)
+  // for this lane's rows, bits past NK cleared; a virtual block's are 0.
+  // MK: the mask words of the rows of this lane for two tiles in flight:
+  // mt[slot][j][half] for tile position p in slot p % 2, bits past NK
+  // cleared (a virtual tile's are 0).  A tile's words are fetched with its
+  // K copy, two steps before the first block of the tile is masked.
+  uint32_t mt[2][NQB][2];
+  uint32_t mtk[2][2];                     // per slot and half: bits < NK
+  auto fetch_mask_tile = [&](int kvt, bool full, uint32_t (&d)[NQB][2],
+                             uint32_t (&dk)[2]) {
+    // The words are only combined with their keep masks when used, so the
+    // loads stay in flight; a tile every row sees whole needs none, and a
+    // virtual tile keeps nothing.
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int kvb = kvt + BC * hb;
+      const int kin = NK - kvb;
+      dk[hb] = kin >= 32 ? ~0u : (kin > 0 ? (1u << kin) - 1u : 0u);
+    }
+    if (full) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) d[j][hb] = ~0u;
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int wi = min((kvt + BC * hb) >> 5, a.mw - 1);
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) d[j][hb] = mrow[j][wi];
+      }
+    }
+  };
+  // Whether block blk needs the mask applied: MK, unless every lane's rows
+  // see all of its keys (a wave-uniform test on the loaded words).
+  auto block_masked = [&](int blk) {
+    if constexpr (MK) {
+      bool full = true;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) full = full && mwv[j] == ~0u;
+      return __builtin_amdgcn_ballot_w64(!full) != 0;
+    } else {
+      return masked_at(blk);
+    }
   };
 
   // Exact step for a block whose P (formed with the held m) has a lane sum
@@ -586,7 +834,14 @@ fwd_bf16_kernel(const FwdArgs a) {
   constexpr int NVF = 2 * G::NDB;       // V fragments per step
 
   auto wait_copies_and_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
+    if constexpr (MK) {
+      // The 2 NQB mask-word loads issued after the last tile copies may
+      // stay in flight (memory loads complete in order).
+      static_assert(2 * NQB <= 15, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NQB));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: any
+    }
     __syncthreads();
   };
 
@@ -598,7 +853,11 @@ fwd_bf16_kernel(const FwdArgs a) {
     mfma_pv_acc(v8, pb, acc);
   };
 
-  static_assert(NCOPY + 1 <= NSL, "one copy per issue slot after the first");
+  // Copies of a SYNC step: CPS per issue slot from slot 1 on (NCS slots),
+  // then (MK) the mask words of K's new tile.
+  constexpr int CPS = (NCOPY + NSL - 3) / (NSL - 2);
+  constexpr int NCS = (NCOPY + CPS - 1) / CPS;
+  static_assert(NCS + 2 <= NSL, "copies and mask words fit the issue slots");
   static_assert(G::NKS - KPF == NVF - VPF,
                 "K and V read-ahead cross into the next step in one slot");
   // Step blk of the three-stage pipeline.  On entry `s` holds the (masked)
@@ -625,8 +884,9 @@ fwd_bf16_kernel(const FwdArgs a) {
                   const uint4* kr, const uint4* vr, const uint4* kw,
                   const uint4* vw, const uint4* krn, const uint4* vrn,
                   auto kh_tag, auto vh_tag, auto khn_tag, auto vhn_tag,
-                  auto sync_tag, auto pv_tag, auto nsync_tag) {
+                  auto sync_tag, auto pv_tag, auto nsync_tag, auto ms_tag) {
     constexpr int KH = decltype(kh_tag)::value;
+    constexpr int MS = decltype(ms_tag)::value;   // MK: mask-word slot
     constexpr int VH = decltype(vh_tag)::value;
     constexpr int KHN = decltype(khn_tag)::value;
     constexpr int VHN = decltype(vhn_tag)::value;
@@ -640,6 +900,14 @@ fwd_bf16_kernel(const FwdArgs a) {
     // formed after the first MFMA has been issued.
     const int tile = (blk - 1) >> 1;
     __amdgpu_buffer_rsrc_t rk, rv;
+    int kvk = 0;                        // MK: first key of K's new tile
+    bool fullk = true;                  // MK: every row sees it whole
+    // MK: mask words of block blk+1 (masked at the end of this step).
+    // MK: the mask words of block blk+1 (tile slot MS, half KH).
+    if constexpr (MK) {
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) mwv[j] = mt[MS][j][KH] & mtk[MS][KH];
+    }
     float mu[NQB];
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
@@ -647,7 +915,7 @@ fwd_bf16_kernel(const FwdArgs a) {
       // that fully masked blocks give p = 0 instead of NaN; the first block
       // in which it sees a key takes the exact step (sum test below), which
       // sets m from that block.
-      if constexpr (VL)
+      if constexpr (VM)
         mu[j] = (m_run[j] == -__builtin_inff()) ? 0.f : m_run[j];
       else
         mu[j] = m_run[j];
@@ -685,15 +953,32 @@ fwd_bf16_kernel(const FwdArgs a) {
       }
       if constexpr (SYNC) {
         if (i == 0) {
-          rk = rsrc_at(kp, (tile + 2) * BT);
-          rv = rsrc_at(vp, (tile + 1) * BT);
+          if constexpr (MK) {
+            kvk = tkv(tile + 2);
+            fullk = tfull(tile + 2);
+            rk = rsrc_at(kp, kvk);
+            rv = rsrc_at(vp, tkv(tile + 1));
+          } else {
+            rk = rsrc_at(kp, tkv(tile + 2));
+            rv = rsrc_at(vp, tkv(tile + 1));
+          }
         }
         if constexpr (SERIAL_COPIES) {
           if (i == 1) wait_copies_and_sync();
         }
-        if (i >= 1 && i <= NCOPY) copy_nth(i - 1, rk, rv, kw, vw);
+        if (i >= 1 && i <= NCS) {
+#pragma unroll
+          for (int c = 0; c < CPS; ++c)
+            if ((i - 1) * CPS + c < NCOPY)
+              copy_nth((i - 1) * CPS + c, rk, rv, kw, vw);
+        }
         if constexpr (SERIAL_COPIES) {
-          if (i == NCOPY) wait_copies_and_sync();
+          if (i == NCS) wait_copies_and_sync();
+        }
+        // MK: the mask words of K's tile, after its copies.
+        if constexpr (MK) {
+          if (i == NCS + 1)
+            fetch_mask_tile(kvk, fullk, mt[1 - MS], mtk[1 - MS]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -754,7 +1039,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     for (int j = 0; j < NQB; ++j) {
       ls[j] = lse_[j] + lso_[j];
       bad = bad || !(ls[j] <= TAU_EXP2);
-      if constexpr (VL)
+      if constexpr (VM)
         bad = bad || (m_run[j] == -__builtin_inff() && svis[j]);
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0) exact_block(s, w, ls);  // rare
@@ -772,10 +1057,10 @@ fwd_bf16_kernel(const FwdArgs a) {
       bool vn[NQB];
 #pragma unroll
       for (int j = 0; j < NQB; ++j) vn[j] = true;
-      if (masked_at(blk + 1)) apply_mask(sn, (blk + 1) * BC, vn);
+      if (block_masked(blk + 1)) apply_mask(sn, (blk + 1) * BC, vn);
 #pragma unroll
       for (int j = 0; j < NQB; ++j) s[j] = sn[j];
-      if constexpr (VL) {
+      if constexpr (VM) {
 #pragma unroll
         for (int j = 0; j < NQB; ++j) svis[j] = vn[j];
       }
@@ -804,7 +1089,14 @@ fwd_bf16_kernel(const FwdArgs a) {
         0, 0, 0);
 #pragma unroll
   for (int j = 0; j < NQB; ++j) svis[j] = true;
-  if (masked_at(0)) apply_mask(s, 0, svis);
+  if constexpr (MK) {
+    // Tiles 0 and 1 into slots 0 and 1; block 0 is tile 0, half 0.
+    fetch_mask_tile(tkv(0), tfull(0), mt[0], mtk[0]);
+    fetch_mask_tile(tkv(1), tfull(1), mt[1], mtk[1]);
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) mwv[j] = mt[0][j][0] & mtk[0][0];
+  }
+  if (block_masked(0)) apply_mask(s, 0, svis);
   // Reference max from block 0 (without VL every row sees key 0, so m is
   // finite for the rows that exist; with VL a row may see nothing yet and
   // keep m = -inf).
@@ -829,18 +1121,18 @@ fwd_bf16_kernel(const FwdArgs a) {
   for (int i = 0; i < KPF; ++i) kf[i] = kfrag(Ks0, 1, i);
   // Arguments: K / V stages read, K / V stages written (SYNC steps), the
   // next step's K / V stages, halves read now and next, SYNC, P V, next
-  // step SYNC.
+  // step SYNC, mask-word slot of the block masked at the end of the step.
   step(0, s, pp, kf, vf, Ks0, Vs1, Ks0, Vs0, Ks1, Vs0, Int<1>{}, Int<1>{},
-       Int<0>{}, Int<0>{}, T0{}, T0{}, T1{});
+       Int<0>{}, Int<0>{}, T0{}, T0{}, T1{}, Int<0>{});
   for (int blk = 1; blk <= nsteps; blk += 4) {
     step(blk, s, pp, kf, vf, Ks1, Vs0, Ks0, Vs1, Ks1, Vs0, Int<0>{},
-         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{});
+         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{}, Int<1>{});
     step(blk + 1, s, pp, kf, vf, Ks1, Vs0, Ks0, Vs1, Ks0, Vs1, Int<1>{},
-         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{});
+         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{}, Int<1>{});
     step(blk + 2, s, pp, kf, vf, Ks0, Vs1, Ks1, Vs0, Ks0, Vs1, Int<0>{},
-         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{});
+         Int<0>{}, Int<1>{}, Int<1>{}, T1{}, T1{}, T0{}, Int<0>{});
     step(blk + 3, s, pp, kf, vf, Ks0, Vs1, Ks1, Vs0, Ks1, Vs0, Int<1>{},
-         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{});
+         Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{}, Int<0>{});
   }
 
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
@@ -894,6 +1186,7 @@ static hipError_t launch(const FwdArgs& a, int grid, hipStream_t stream) {
 // template with 8 waves of 32 rows, per-sequence offsets and window
 // masks.  a.nqb covers the longest query sequence.
 hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream) {
+  constexpr int BR = Waves<1>::BR;
   a.nqb = static_cast<int>((static_cast<long long>(max_q) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
@@ -905,7 +1198,33 @@ hipError_t launch_fwd_varlen_bf16(FwdArgs a, int max_q, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Forward under an arbitrary visibility bit mask (d = 128): the non-causal
+// configuration over the listed key tiles with per-block mask words.
+// a.total_q / a.total_k are Nq / Nk.
+hipError_t launch_fwd_masked_bf16(FwdArgs a, hipStream_t stream) {
+  // 128 query rows per workgroup, so that a workgroup streams the tiles its
+  // own 128 rows see (not the union over 256), as four waves of 32 rows:
+  // two workgroups per CU (LDS) give two waves per SIMD.  Measured against
+  // two waves of 64 rows (one per SIMD) on B4 H16 N8192: block-sparse
+  // 0.507 -> 0.470 ms, all-visible 2.047 -> 1.981, causal-shaped 1.194 ->
+  // 1.128, 50% random 2.454 -> 2.289.
+  using W = Waves<1, 4>;
+  a.nqb = static_cast<int>((static_cast<long long>(a.total_q) + W::BR - 1) /
+                           W::BR);
+  const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
+  if (grid > 0x7FFFFFFFLL || a.total_k > MASK_MAX_NK)
+    return hipErrorInvalidConfiguration;
+  if (static_cast<long long>(a.total_k) * 128 * 2 > 0x7FFFFFFFLL)
+    return hipErrorInvalidConfiguration;
+  a.mw = (a.total_k + 31) / 32;
+  a.xcd_chunk = grid % 8 == 0;
+  hipLaunchKernelGGL((fwd_bf16_kernel<128, false, 1, false, true, 4>),
+                     dim3((int)grid), dim3(W::NTHR), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
+  constexpr int BR = Waves<2>::BR;
   a.nqb = static_cast<int>((static_cast<long long>(a.N) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;

@@ -242,8 +242,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
  *   mask[b * mask_batch_stride + h * mask_head_stride + i * W + j / 32] is
  *   set, W = ceil(Nk / 32); the softmax runs over the visible keys only and
  *   a row that sees no key gets o = 0 and lse = -inf.  Work follows the
- *   mask: a 32-key tile is loaded and computed for a block of 128 query
- *   rows only if one of them sees one of its keys.
+ *   mask: a 64-key tile is loaded and computed for a block of 128 query
+ *   rows only if one of them sees one of its keys, and its mask words are
+ *   only read if some row of the block does not see all of them.
  *   q, o      device, bfloat16 [B][H][Nq][d] (q read only, o written).
  *   k, v      device, bfloat16 [B][Hkv][Nk][d] (read only).
  *   lse       device, float [B][H][Nq] (written, natural log).

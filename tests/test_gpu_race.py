@@ -30,6 +30,9 @@ def _serial_lib():
     lib.fa_fwd_fp8.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 10 + [f32, vp]
     lib.fa_fwd_varlen.restype = i32
+    i64 = ctypes.c_longlong
+    lib.fa_fwd_masked.argtypes = [vp] * 6 + [i64, i64] + [i32] * 6 + [f32, vp]
+    lib.fa_fwd_masked.restype = i32
     return lib
 
 
@@ -101,6 +104,37 @@ def test_varlen_forward_serial_equals_pipelined():
                              o2.data_ptr(), l2.data_ptr(), cu.data_ptr(),
                              cu.data_ptr(), len(lens), H, Hkv, tot, tot,
                              max(lens), 128, 1, 1000, -1, 128 ** -0.5,
+                             _stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("kind", ["block_sparse", "random", "causal"])
+def test_masked_forward_serial_equals_pipelined(kind):
+    """The masked configuration (128-row workgroups over the listed key
+    tiles, mask words fetched with the K copies): block-sparse (whole
+    tiles), random (every tile partial) and causal-shaped masks, a ragged
+    key count and a shared mask."""
+    import torch
+    import exact_attention_101_amd as fa
+    B, H, Hkv, Nq, Nk = 2, 4, 2, 700, 1000
+    q = workloads.draw((B, H, Nq, 128), 8300)
+    k = workloads.draw((B, Hkv, Nk, 128), 8301)
+    v = workloads.draw((B, Hkv, Nk, 128), 8302)
+    qb, kb, vb = (workloads.to_bf16(x).to(dev()) for x in (q, k, v))
+    if kind == "block_sparse":
+        m = workloads.block_sparse_mask(Nq, Nk, 128, 2, 8303)
+    elif kind == "random":
+        m = workloads.random_mask((Nq, Nk), 0.3, 8304)
+    else:
+        m = np.tril(np.ones((Nq, Nk), dtype=bool), k=Nk - Nq)
+    mw = torch.from_numpy(workloads.pack_mask(m).view(np.int32)).to(dev())
+    o1, l1 = fa.forward_masked(qb, kb, vb, mw[None, None])
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    lib = _serial_lib()
+    assert lib.fa_fwd_masked(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(),
+                             o2.data_ptr(), l2.data_ptr(), mw.data_ptr(), 0,
+                             0, B, H, Hkv, Nq, Nk, 128, 128 ** -0.5,
                              _stream()) == 0
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
