@@ -676,7 +676,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d128"),
-            "kernel": "fwd_bf16_kernel<128, false, 2, false>",
+            "kernel": "fwd_bf16_kernel<128, false, 2, false, false, 4>",
             "flops_per_launch": w.flops,
             "peak_basis": f"{cus} CUs x 4096 bf16 FLOP/clk x 2.4 GHz",
         },
