@@ -1042,7 +1042,8 @@ fwd_bf16_kernel(const FwdArgs a) {
       if constexpr (VM)
         bad = bad || (m_run[j] == -__builtin_inff() && svis[j]);
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) exact_block(s, w, ls);  // rare
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0))
+      exact_block(s, w, ls);  // rare
 #pragma unroll
     for (int j = 0; j < NQB; ++j) l_run[j] += ls[j];
 #pragma unroll
@@ -1057,7 +1058,8 @@ fwd_bf16_kernel(const FwdArgs a) {
       bool vn[NQB];
 #pragma unroll
       for (int j = 0; j < NQB; ++j) vn[j] = true;
-      if (block_masked(blk + 1)) apply_mask(sn, (blk + 1) * BC, vn);
+      if (__builtin_expect(block_masked(blk + 1), 0))
+        apply_mask(sn, (blk + 1) * BC, vn);
 #pragma unroll
       for (int j = 0; j < NQB; ++j) s[j] = sn[j];
       if constexpr (VM) {
