@@ -182,6 +182,14 @@ PROBE_BODIES = {
     "mfma_bf16+dot2": (18, 4, "bf16 MFMA, each with 4 v_dot2c_f32_bf16"),
     "mfma_bf16+mov64": (19, 4, "bf16 MFMA, each with 4 v_mov_b64"),
     "cvt_scalef32_pk_fp8": (20, 16, "v_cvt_scalef32_pk_fp8_f32"),
+    "slot_bf16": (21, 4, "the bf16 forward's issue slot: scores MFMA, 2 x "
+                         "(fma -> exp), P V MFMA, cvt_pk_bf16 + 2 add of the "
+                         "exponentials (counted per slot)"),
+    "lds_k": (22, 8, "ds_read_b128 at the bf16 forward's K fragment "
+                     "addresses"),
+    "lds_v": (23, 16, "ds_read_b64_tr_b16 at the bf16 forward's V fragment "
+                      "addresses"),
+    "lds_tr_seq": (24, 16, "ds_read_b64_tr_b16 at consecutive 8-byte units"),
 }
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
@@ -199,6 +207,9 @@ PROBE_CONFIGS = (
     + [("mfma_bf16", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain",
                                           "dot2_bf16", "mov_b64")]
     + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
+    + [("slot_bf16", "idle", 4 * n, n) for n in (1, 2)]
+    + [(b, "idle", 4 * n, n) for n in (1, 2, 4)
+       for b in ("lds_k", "lds_v", "lds_tr_seq")]
 )
 
 

@@ -30,6 +30,8 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
 
 enum Body {
   B_IDLE = 0,     // no work
@@ -59,6 +61,18 @@ enum Body {
   B_MFMA16_DOT2 = 18,  // 4 x (bf16 MFMA + 4 v_dot2c_f32_bf16)
   B_MFMA16_MOV64 = 19, // 4 x (bf16 MFMA + 4 v_mov_b64)
   B_CVT8S = 20,        // 16 x v_cvt_scalef32_pk_fp8_f32
+  // The bf16 forward's issue slot, 4 per round: scores MFMA (vector
+  // accumulator), 2 x (v_fma_f32 -> v_exp_f32), P V MFMA (accumulation
+  // registers), then v_cvt_pk_bf16_f32 and 2 v_add_f32 of the two
+  // exponentials.
+  B_SLOT16 = 21,
+  // LDS reads of the bf16 forward, one wave's share of a 32-key step:
+  // 8 x ds_read_b128 at the K fragment addresses, 16 x ds_read_b64_tr_b16
+  // at the V fragment addresses, 16 x ds_read_b64_tr_b16 at 64 consecutive
+  // 8-byte units (no two lanes of a 16-lane group in one bank group).
+  B_LDS_K = 22,
+  B_LDS_V = 23,
+  B_LDS_TRSEQ = 24,
 };
 
 struct Regs {
@@ -68,6 +82,9 @@ struct Regs {
   double dd[8], dsrc;       // 64-bit move targets and source (B_*MOV64)
   f32x16_t acc[4];
   i32x8_t da[2], db[2];     // data operands (B_MFMA*_DATA)
+  float lsum;               // B_SLOT16 lane sum
+  float cs;                 // B_SLOT16 scale (uniform)
+  const uint8_t* lds;       // B_LDS_*: the workgroup's LDS reserve
 };
 
 __device__ __forceinline__ void fma16(Regs& r, int first, int n) {
@@ -225,6 +242,76 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
           mov64(r, i);
       }
     }
+  } else if constexpr (BODY == B_SLOT16) {
+    // Phases fenced as in the forward kernel; the scale is an opaque
+    // scalar, so the FMAs read fixed inputs without being hoisted.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float cs = r.cs;
+      asm volatile("" : "+s"(cs));
+      __builtin_amdgcn_sched_barrier(0);
+      r.acc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a16, a16, r.acc[j & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(r.x[2 * j], cs, -r.z));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(r.x[2 * j + 1], cs, -r.z));
+      asm volatile("" : "+v"(r.acc[j & 1]));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(r.acc[2 + (j & 1)])
+                   : "v"(a16), "v"(a16));
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x2_t pk = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+      r.w[j] = __builtin_bit_cast(int, pk);
+      r.lsum += e0 + e1;
+      asm volatile("" : "+v"(r.w[j]), "+v"(r.lsum));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (BODY == B_LDS_K || BODY == B_LDS_V ||
+                       BODY == B_LDS_TRSEQ) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+    typedef __attribute__((address_space(3))) short4_t lds_s4;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 31, hh = lane >> 5;
+    if constexpr (BODY == B_LDS_K) {
+      // Rows of 17 16-byte slots; lane row sigma(li), chunk 8 hh + s.
+      const int m = li;
+      const int sg = (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+      const int base = (sg * 17 + hh * 8) * 16;
+      u32x4_t k[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        k[i] = *(lds_u4*)(r.lds + base + 16 * i);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(k[i]));
+    } else {
+      int base;
+      if constexpr (BODY == B_LDS_V) {
+        // Unpadded 256-byte rows, 64-byte segment XOR (row % 4).
+        const int R = (lane >> 2) & 3, j = lane & 3;
+        const int row = 8 * hh + R;
+        const int ch = 4 * (row & 3) + 2 * ((lane >> 4) & 1) + (j & 1);
+        base = (row * 16 + ch) * 16 + 8 * (j >> 1);
+      } else {
+        base = 8 * lane;
+      }
+      short4_t v[16];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int off = BODY == B_LDS_V
+                              ? ((base ^ ((f % 4) << 6)) +
+                                 (16 * (f / 4) + 4 * hf) * 256)
+                              : base + 512 * (2 * f + hf);
+          v[2 * f + hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4*)(r.lds + off));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[i]));
+    }
   } else if constexpr (BODY == B_EXP_CHAIN) {
     // The softmax's dependent sequence: scale and shift, exponential, sum.
     // Written with builtins so that the compiler inserts the wait states a
@@ -265,6 +352,9 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
 #pragma unroll
   for (int i = 0; i < 8; ++i) r.dd[i] = seed * i;
   r.dsrc = seed;
+  r.lsum = 0.f;
+  r.cs = 0.999f;
+  r.lds = reinterpret_cast<const uint8_t*>(reserve);
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
   // Data operands: lane-dependent fragments of the caller's 512-entry
@@ -301,6 +391,7 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.dd[i]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) sink += r.acc[j][lane & 15];
+  sink += r.lsum;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     sink += static_cast<float>(r.da[j][lane & 7] ^ r.db[j][lane & 7]);
@@ -360,6 +451,10 @@ launch_fn pick_alone(int a) {
     case B_MFMA16_ADD: return launch<B_MFMA16_ADD, B_IDLE>;
     case B_MFMA16_DOT2: return launch<B_MFMA16_DOT2, B_IDLE>;
     case B_MFMA16_MOV64: return launch<B_MFMA16_MOV64, B_IDLE>;
+    case B_SLOT16: return launch<B_SLOT16, B_IDLE>;
+    case B_LDS_K: return launch<B_LDS_K, B_IDLE>;
+    case B_LDS_V: return launch<B_LDS_V, B_IDLE>;
+    case B_LDS_TRSEQ: return launch<B_LDS_TRSEQ, B_IDLE>;
     default: return nullptr;
   }
 }
@@ -384,6 +479,10 @@ launch_fn pick(int a, int b) {
     case B_MFMA16_ADD: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_DOT2: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;
+    case B_SLOT16:
+    case B_LDS_K:
+    case B_LDS_V:
+    case B_LDS_TRSEQ: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_DATA:
     case B_MFMA8_DATA: return b == B_IDLE ? pick_alone(a) : nullptr;
     default: return nullptr;

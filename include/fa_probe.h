@@ -29,10 +29,17 @@ extern "C" {
  *           turn, 14 v_dot2c_f32_bf16, 15 v_mov_b64, 16 v_cvt_pk_bf16_f32,
  *           17 / 18 / 19 bf16 MFMA each followed by 4 v_add_f32 / 4
  *           v_dot2c_f32_bf16 / 4 v_mov_b64 in the same wave, 20
- *           v_cvt_scalef32_pk_fp8_f32; b may also be 0, idle, and must be
- *           for bodies 12, 13 and 17 to 19).
+ *           v_cvt_scalef32_pk_fp8_f32, 21 the bf16 forward's issue slot
+ *           (scores MFMA, two v_fma_f32 -> v_exp_f32, P V MFMA into
+ *           accumulation registers, v_cvt_pk_bf16_f32 and two v_add_f32),
+ *           22 ds_read_b128 at the bf16 forward's K fragment addresses, 23
+ *           ds_read_b64_tr_b16 at its V fragment addresses, 24
+ *           ds_read_b64_tr_b16 at consecutive 8-byte units; b may also be
+ *           0, idle, and must be for bodies 12, 13, 17 to 19 and 21 to
+ *           24).
  *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
- *           CU, so waves / 4 waves on each SIMD).
+ *           CU, so waves / 4 waves on each SIMD; bodies 22 to 24 read the
+ *           workgroup's 96 KiB LDS reserve, shared by its waves).
  *   na      the first 4 * na waves run body a, the others body b.
  *   iters   rounds of the body per wave, >= 1.
  *   grid    workgroups (the CU count for one per CU).

@@ -66,7 +66,9 @@ def test_probe_library_exports_its_header():
     assert f(12, 0, 4, 1, 8, 1, A, M, None) == 1         # data misaligned
     assert f(13, 1, 8, 1, 8, 1, A, A, None) == 1         # data body mixed
     assert f(18, 1, 8, 1, 8, 1, A, None, None) == 1      # same-wave mix mixed
-    assert f(21, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
+    assert f(21, 1, 8, 1, 8, 1, A, None, None) == 1      # slot body mixed
+    assert f(23, 2, 8, 1, 8, 1, A, None, None) == 1      # LDS body mixed
+    assert f(25, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
 
 
 def test_version_and_status_strings(lib):
