@@ -480,22 +480,28 @@ fwd_bf16_kernel(const FwdArgs a) {
   }
   // MK: the list is read through two 64-entry windows in registers (lane L
   // holds entries 64 w0 + L and 64 (w0 + 1) + L), so that a tile's entry
-  // comes from v_readlane and not from an LDS read the wave must wait for;
-  // positions are asked for in increasing order, so the windows move on
-  // once every 64 tiles.
+  // comes from v_readlane and not from an LDS read the wave must wait for.
+  // Positions are asked for in increasing order; the windows move on (once
+  // every 64 tiles) just before the barrier that precedes each copy step,
+  // which also waits for that LDS read, so a lookup has no read behind it
+  // (one could only be waited for together with every fragment read in
+  // flight).
   int win0 = 0, win1 = 0, w0 = 0;
   if constexpr (MK) {
     win0 = tl[lane];
     win1 = tl[64 + lane];
   }
-  // Entry of tile position t < ntl (MK).
-  auto entry = [&](int t) -> int {
-    while ((t >> 6) >= w0 + 2) {              // rare: next window
+  // MK: move the windows on until they hold position tmax.
+  auto advance_list = [&](int tmax) {
+    while ((tmax >> 6) >= w0 + 2) {           // rare: next window
       win0 = win1;
       const int i = 64 * (w0 + 2) + lane;
       win1 = i < NTL ? tl[i] : 0;
       ++w0;
     }
+  };
+  // Entry of tile position t < ntl (MK), 64 w0 <= t < 64 (w0 + 2).
+  auto entry = [&](int t) -> int {
     return __builtin_amdgcn_readlane((t >> 6) == w0 ? win0 : win1, t & 63);
   };
   // First key of tile position t (MK: of the t-th listed tile; positions
@@ -833,8 +839,11 @@ fwd_bf16_kernel(const FwdArgs a) {
   constexpr int VPF = 2;                // V fragments read ahead
   constexpr int NVF = 2 * G::NDB;       // V fragments per step
 
-  auto wait_copies_and_sync = [&]() {
+  // tmax (MK): the largest tile position the next step looks up, if that
+  // is a copy step (else -1).
+  auto wait_copies_and_sync = [&](int tmax) {
     if constexpr (MK) {
+      if (tmax >= 0) advance_list(tmax);
       // The 2 NQB mask-word loads issued after the last tile copies may
       // stay in flight (memory loads complete in order).
       static_assert(2 * NQB <= 15, "vmcnt field");
@@ -947,7 +956,9 @@ fwd_bf16_kernel(const FwdArgs a) {
             as_bf16x8(kcur), qf[qb][f], sn[qb], 0, 0, 0);
         if (qb == 0 && f + KPF >= G::NKS) {
           // First read of the next step's stage (V's follows in this slot).
-          if (NSYNC && f + KPF == G::NKS) wait_copies_and_sync();
+          // The next step (blk + 1) is a copy step: it looks up tile
+          // positions blk / 2 + 1 and blk / 2 + 2.
+          if (NSYNC && f + KPF == G::NKS) wait_copies_and_sync(blk / 2 + 2);
           kf[f % KPF] = kfrag(krn, KHN, f + KPF - G::NKS);
         }
       }
@@ -964,7 +975,7 @@ fwd_bf16_kernel(const FwdArgs a) {
           }
         }
         if constexpr (SERIAL_COPIES) {
-          if (i == 1) wait_copies_and_sync();
+          if (i == 1) wait_copies_and_sync(-1);
         }
         if (i >= 1 && i <= NCS) {
 #pragma unroll
@@ -973,7 +984,7 @@ fwd_bf16_kernel(const FwdArgs a) {
               copy_nth((i - 1) * CPS + c, rk, rv, kw, vw);
         }
         if constexpr (SERIAL_COPIES) {
-          if (i == NCS) wait_copies_and_sync();
+          if (i == NCS) wait_copies_and_sync(-1);
         }
         // MK: the mask words of K's tile, after its copies.
         if constexpr (MK) {
@@ -1080,7 +1091,7 @@ fwd_bf16_kernel(const FwdArgs a) {
   copy_k(0, Ks0);
   copy_v(0, Vs0);
   copy_k(1, Ks1);
-  wait_copies_and_sync();
+  wait_copies_and_sync(-1);
   f32x16_t s[NQB];
 #pragma unroll
   for (int j = 0; j < NQB; ++j) s[j] = f32x16_t{};
