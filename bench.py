@@ -520,6 +520,38 @@ def main() -> int:
             "flops": "2.5 x forward (10 B H N^2 d)"}
         _progress(f"bf16_n8192_backward: {extras['bf16_n8192_backward']}")
         del dout, dq, dk, dv, ws
+        # Context for the HBM-bound rows: the read bandwidth a plain
+        # streaming kernel reaches on this card (4 GiB read once per launch,
+        # eight 16-byte loads in flight per thread, 64 workgroups per CU,
+        # the best of 2-64 measured; fa_probe_read).
+        read_gbs = None
+        probe_r = os.path.join(os.path.dirname(fa.__file__), "libfa_probe.so")
+        if os.path.exists(probe_r):
+            import ctypes
+            rlib = ctypes.CDLL(probe_r)
+            rlib.fa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong,
+                                           ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+            rlib.fa_probe_read.restype = ctypes.c_int
+            rbuf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+            rgrid = 64 * torch.cuda.get_device_properties(0).multi_processor_count
+            rsink = torch.zeros(rgrid, dtype=torch.int32, device=dev)
+            rstream = torch.cuda.current_stream().cuda_stream
+
+            def _read_once():
+                rc = rlib.fa_probe_read(rbuf.data_ptr(), rbuf.numel(), rgrid,
+                                        rsink.data_ptr(), rstream)
+                if rc != 0:
+                    raise RuntimeError(f"fa_probe_read = {rc}")
+
+            tm_r = _time_launches(_read_once, 10, 5, min_warm_ms=30.0)
+            read_gbs = rbuf.numel() / (tm_r["mean"] * 1e-3) / 1e9
+            extras["hbm_read_probe_4gib"] = {
+                "ms": round(tm_r["mean"], 4), "GB/s": round(read_gbs, 1),
+                "frac_of_hbm_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+                "what": "one streaming read of 4 GiB (fa_probe_read)"}
+            _progress(f"hbm_read_probe_4gib: {extras['hbm_read_probe_4gib']}")
+            del rbuf, rsink
         # Decode at long context through the split-KV forward: one query
         # per head, 32 query heads on 8 KV heads, 65536 keys, B = 8.  Bound
         # by HBM: K and V are read once (the algorithmic bytes).
@@ -541,6 +573,7 @@ def main() -> int:
             "ms": round(tm_d["mean"], 4), "ms_median": round(tm_d["median"], 4),
             "ms_min": round(tm_d["min"], 4), "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "frac_of_read_probe": round(gbs / read_gbs, 4) if read_gbs else None,
             "num_splits": ns, "bytes": "K and V once"}
         _progress(f"decode_b8_h32_hkv8_nk65536: {extras['decode_b8_h32_hkv8_nk65536']}")
         del qd, kd, vd, od, ld, wd

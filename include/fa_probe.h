@@ -58,6 +58,24 @@ extern "C" {
 int fa_probe_rates(int a, int b, int waves, int na, int iters, int grid,
                    unsigned long long* out, const void* data, void* stream);
 
+/*
+ * fa_probe_read -- one launch that reads `bytes` of device memory once
+ * (HBM read bandwidth available to a streaming kernel, the ceiling of the
+ * decode path's K/V reads).
+ *   src     device, 16-byte aligned, bytes readable (read only; contents
+ *           do not matter).
+ *   bytes   a positive multiple of 16.
+ *   grid    workgroups of 256 threads, >= 1 (each thread keeps eight
+ *           16-byte loads in flight, grid-stride over the buffer).
+ *   sink    device, caller-owned, grid unsigned words; word g is written
+ *           only if workgroup g's threads read a fixed bit pattern.
+ *   stream  hipStream_t or NULL; one kernel is enqueued.
+ *   Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the
+ *   launch failed.
+ */
+int fa_probe_read(const void* src, unsigned long long bytes, int grid,
+                  unsigned* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,8 +52,21 @@ def test_probe_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "fa_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["fa_probe_rates"]
+    assert names == ["fa_probe_rates", "fa_probe_read"]
     plib = ctypes.CDLL(build.PROBE_LIB)
+    for n in names:
+        assert hasattr(plib, n), n
+    r = plib.fa_probe_read
+    r.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    r.restype = ctypes.c_int
+    S = ctypes.c_void_p(0x2000)                          # never dereferenced
+    assert r(None, 1 << 20, 8, S, None) == 1             # null source
+    assert r(S, 1 << 20, 8, None, None) == 1             # null sink
+    assert r(S, 0, 8, S, None) == 1                      # nothing to read
+    assert r(S, (1 << 20) + 8, 8, S, None) == 1          # not 16-byte units
+    assert r(ctypes.c_void_p(0x2008), 1 << 20, 8, S, None) == 1  # misaligned
+    assert r(S, 1 << 20, 0, S, None) == 1                # empty grid
     f = plib.fa_probe_rates
     f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 3
     f.restype = ctypes.c_int
