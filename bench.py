@@ -476,10 +476,19 @@ def main() -> int:
     _progress(f"{w.name}: {ms:.4f} ms, {tflops:.1f} TFLOP/s")
     # The clock the card runs this kernel at (power-limited): amd-smi samples
     # while the same launches run back to back for a second.
-    clock = _under_load(step, 1.0)
+    clock = _under_load(step, 3.0)
     if clock is not None:
-        clock["frac_of_peak_at_that_clock"] = round(
-            tflops / (BF16_PEAK_TFLOPS * clock["gfx_mhz"] / 2400.0), 4)
+        frac_clk = tflops / (BF16_PEAK_TFLOPS * clock["gfx_mhz"] / 2400.0)
+        if frac_clk <= 1.0:
+            clock["frac_of_peak_at_that_clock"] = round(frac_clk, 4)
+        else:
+            # The samples cannot describe the timed launches (more than the
+            # whole matrix rate at that clock): amd-smi reported values from
+            # before the load.
+            clock["frac_of_peak_at_that_clock"] = None
+            clock["inconsistent"] = (
+                f"{frac_clk:.2f} of the peak at the sampled clock: the "
+                "samples predate the load")
     _progress(f"clock under load: {clock}")
 
     extras = {}
