@@ -442,7 +442,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the forward kernel runs on a "
-              f"single device and this build has no multi-GPU path "
+              f"single device and this library has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         return 2
     rank = int(os.environ.get("RANK", "0"))
