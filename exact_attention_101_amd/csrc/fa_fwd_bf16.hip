@@ -332,18 +332,28 @@ fwd_bf16_kernel(const FwdArgs a) {
       static_cast<const uint16_t*>(a.v) + (krow0 + kv_begin) * D;
 
   // ---- Q -> registers (B operand of S^T = K Q^T), NQB query blocks ----
+  // All of the wave's Q loads are issued here; the fragments move to the
+  // accumulation registers only after the prologue's tile copies are
+  // issued (below), so the Q loads and the copies wait together once,
+  // instead of each load waiting in turn.
   bf16x8_t qf[NQB][G::NKS];
-  {
+  uint4 qraw[NQB][G::NKS];
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const int row = qw0 + 32 * j + li;
+    const bool ok = row < NQ;
+    const uint16_t* src = qp + static_cast<int64_t>(ok ? row : NQ - 1) * D +
+                          h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < G::NKS; ++s) qraw[j][s] = keep_if(ldg16(src + 8 * s), ok);
+  }
+  auto settle_q = [&]() {
     const uint32_t flip = a.neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
-      const int row = qw0 + 32 * j + li;
-      const bool ok = row < NQ;
-      const uint16_t* src = qp + static_cast<int64_t>(ok ? row : NQ - 1) * D +
-                            h * (D / 2);
 #pragma unroll
       for (int s = 0; s < G::NKS; ++s) {
-        uint4 u = keep_if(ldg16(src + 8 * s), ok);
+        uint4 u = qraw[j][s];
         u.x ^= flip; u.y ^= flip; u.z ^= flip; u.w ^= flip;
         qf[j][s] = as_bf16x8(u);
         // Q is only ever an MFMA operand, which MFMA reads from
@@ -352,7 +362,7 @@ fwd_bf16_kernel(const FwdArgs a) {
         asm volatile("" : "+a"(qf[j][s]));
       }
     }
-  }
+  };
 
   // ---- MK: the 64-key tiles some row of the workgroup sees ----
   // Each wave ORs the mask rows q0 + wave, q0 + wave + NWAVE, ... word by
@@ -1091,6 +1101,7 @@ fwd_bf16_kernel(const FwdArgs a) {
   copy_k(0, Ks0);
   copy_v(0, Vs0);
   copy_k(1, Ks1);
+  settle_q();
   wait_copies_and_sync(-1);
   f32x16_t s[NQB];
 #pragma unroll
