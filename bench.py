@@ -190,6 +190,9 @@ PROBE_BODIES = {
     "lds_v": (23, 16, "ds_read_b64_tr_b16 at the bf16 forward's V fragment "
                       "addresses"),
     "lds_tr_seq": (24, 16, "ds_read_b64_tr_b16 at consecutive 8-byte units"),
+    "exp2_fma": (25, 16, "the FMA-pipe exponential of the fp8 forward's "
+                         "option (8 vector instructions; counted per "
+                         "exponential)"),
 }
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
@@ -199,7 +202,7 @@ PROBE_CONFIGS = (
     [(b, "idle", 4 * n, n) for n in (1, 2, 4)
      for b in ("fma", "exp", "exp+fma", "add", "cvt_pk_fp8", "maximum3",
                "exp_chain", "dot2_bf16", "mov_b64", "cvt_pk_bf16",
-               "cvt_scalef32_pk_fp8")]
+               "cvt_scalef32_pk_fp8", "exp2_fma")]
     + [(b, "idle", 4 * n, n) for n in (1, 2)
        for b in ("mfma_f8", "mfma_bf16", "mfma_f8+exp", "mfma_bf16+exp",
                  "mfma_bf16+add", "mfma_bf16+dot2", "mfma_bf16+mov64")]
@@ -207,6 +210,7 @@ PROBE_CONFIGS = (
     + [("mfma_bf16", b, 8, 1) for b in ("exp", "fma", "exp+fma", "exp_chain",
                                           "dot2_bf16", "mov_b64")]
     + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
+    + [("mfma_f8", "exp2_fma", 8, 1), ("mfma_bf16", "exp2_fma", 8, 1)]
     + [("slot_bf16", "idle", 4 * n, n) for n in (1, 2)]
     + [(b, "idle", 4 * n, n) for n in (1, 2, 4)
        for b in ("lds_k", "lds_v", "lds_tr_seq")]
@@ -664,6 +668,25 @@ def main() -> int:
                            "ms_min": round(tm["min"], 4), "TFLOP/s": round(t, 1),
                            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
             _progress(f"{key}: {extras[key]}")
+            if rot:
+                continue
+            # Part of each tile's exponentials on the FMA pipe
+            # (fa_fwd_fp8_exp2_fma), against v_exp_f32 above: 4, 8 or 16 of
+            # a lane's 16 pairs per 64-key tile.
+            for pairs in (4, 8, 16):
+                tm = _time_launches(
+                    lambda: fa.forward_fp8(q8, k8, v8, desc, out=oo, lse=ll,
+                                           exp2_fma_pairs=pairs),
+                    20, 20, min_warm_ms=30.0)
+                t = ww.flops / (tm["mean"] * 1e-3) / 1e12
+                key = f"fp8_n8192_exp2_fma_{pairs}_of_16_pairs"
+                extras[key] = {
+                    "ms": round(tm["mean"], 4),
+                    "ms_median": round(tm["median"], 4),
+                    "TFLOP/s": round(t, 1),
+                    "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4),
+                    "vs_v_exp_f32": round(m / tm["mean"], 4)}
+                _progress(f"{key}: {extras[key]}")
         mq = _time_launches(lambda: fa.quantize_fp8(xq, signs), 20, 20, min_warm_ms=30.0)["mean"]
         nbytes = xq.numel() * (4 * 2 + 1)      # fp32 read twice, e4m3 write
         extras["fp8_quantize_hadamard_per_tensor"] = {

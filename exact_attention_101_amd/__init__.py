@@ -20,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_kv", "forward_kv_noalloc", "forward_varlen", "forward_masked", "backward", "forward_fp8", "quantize_fp8", "library", "lib_path",
+__all__ = ["forward", "forward_kv", "forward_kv_noalloc", "forward_varlen", "forward_masked", "backward", "forward_fp8", "exp2_fma", "quantize_fp8", "library", "lib_path",
            "FaError", "FA_DTYPE_BF16", "FA_DTYPE_FP8_E4M3"]
 
 FA_DTYPE_BF16 = 0
@@ -59,6 +59,11 @@ def library() -> ctypes.CDLL:
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                    i32, i32, f32, vp, vp]
         lib.fa_fwd_fp8.restype = i32
+        lib.fa_fwd_fp8_exp2_fma.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, i32, f32, vp, i32, vp]
+        lib.fa_fwd_fp8_exp2_fma.restype = i32
+        lib.fa_exp2_fma.argtypes = [vp, vp, i64, vp]
+        lib.fa_exp2_fma.restype = i32
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                i32, i32, i32, i32, i32, f32, vp]
         lib.fa_bwd.restype = i32
@@ -376,9 +381,12 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale=None,
 
 
 def forward_fp8(q8, k8, v8, descale_qkv=None, *, causal: bool = False,
-                scale=None, out=None, lse=None):
+                scale=None, out=None, lse=None, exp2_fma_pairs: int = 0):
     """e4m3 attention forward.  q8/k8/v8: torch.float8_e4m3fn or uint8 codes;
     descale_qkv: device float32 tensor of 3 descales (or None for 1).
+    exp2_fma_pairs (0, 4, 8 or 16): how many of the 16 weight pairs a lane
+    forms per 64-key tile take the FMA-pipe exponential
+    (fa_fwd_fp8_exp2_fma); 0 is fa_fwd_fp8.
     Returns (o bf16, lse fp32)."""
     import torch
     B, H, Hkv, N, d = _shape_check(q8, k8, v8)
@@ -400,12 +408,33 @@ def forward_fp8(q8, k8, v8, descale_qkv=None, *, causal: bool = False,
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     _out_check(lse, "lse", (B, H, N), torch.float32, q8.device)
-    _check(library().fa_fwd_fp8(
-        q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
-        lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
-        descale_qkv.data_ptr() if descale_qkv is not None else None,
-        _stream_handle(q8.device)))
+    desc = descale_qkv.data_ptr() if descale_qkv is not None else None
+    if exp2_fma_pairs:
+        _check(library().fa_fwd_fp8_exp2_fma(
+            q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
+            desc, int(exp2_fma_pairs), _stream_handle(q8.device)))
+    else:
+        _check(library().fa_fwd_fp8(
+            q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), float(scale),
+            desc, _stream_handle(q8.device)))
     return out, lse
+
+
+def exp2_fma(x, *, out=None):
+    """2^x elementwise by the FMA-pipe exponential of the fp8 forward's
+    exp2_fma_pairs option (fa_exp2_fma).  x: contiguous float32 CUDA tensor.
+    Returns a float32 tensor like x."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("exp2_fma expects a contiguous float32 CUDA tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    _out_check(out, "out", x.shape, torch.float32, x.device, align=4)
+    _check(library().fa_exp2_fma(x.data_ptr(), out.data_ptr(), x.numel(),
+                                 _stream_handle(x.device)))
+    return out
 
 
 def quantize_fp8(x, signs=None, *, out=None, amax_descale=None):

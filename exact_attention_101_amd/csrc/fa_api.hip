@@ -11,7 +11,10 @@
 
 namespace fa {
 hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream);
-hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(FwdArgs a, bool causal, int fma_pairs,
+                          hipStream_t stream);
+hipError_t launch_exp2_fma(const float* x, float* y, long long n,
+                           hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, bool causal, hipStream_t stream);
 hipError_t launch_splitkv_bf16(SplitArgs a, bool causal, hipStream_t stream);
 hipError_t splitkv_scratch(float** out);
@@ -117,8 +120,35 @@ FA_EXPORT int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
     return FA_ERR_MISALIGNED;
   fa::FwdArgs a = make_args(q8, k8, v8, o, lse, B, H, Hkv, N, scale);
   a.descale = descale_qkv;
+  return hip_status(fa::launch_fwd_fp8(a, causal != 0, 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_fwd_fp8_exp2_fma(const void* q8, const void* k8,
+                                  const void* v8, void* o, float* lse, int B,
+                                  int H, int Hkv, int N, int d, int causal,
+                                  float scale, const float* descale_qkv,
+                                  int fma_pairs, void* stream) {
+  const int st = check_fwd(q8, k8, v8, o, lse, B, H, Hkv, N, d, causal, scale,
+                           d == 128 && (fma_pairs == 0 || fma_pairs == 4 ||
+                                        fma_pairs == 8 || fma_pairs == 16));
+  if (st != FA_OK) return st;
+  if (descale_qkv && (reinterpret_cast<uintptr_t>(descale_qkv) & 3u))
+    return FA_ERR_MISALIGNED;
+  fa::FwdArgs a = make_args(q8, k8, v8, o, lse, B, H, Hkv, N, scale);
+  a.descale = descale_qkv;
+  return hip_status(fa::launch_fwd_fp8(a, causal != 0, fma_pairs,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_exp2_fma(const float* x, float* y, long long n,
+                          void* stream) {
+  if (!x || !y || n < 0) return FA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(x) & 3u) ||
+      (reinterpret_cast<uintptr_t>(y) & 3u))
+    return FA_ERR_MISALIGNED;
   return hip_status(
-      fa::launch_fwd_fp8(a, causal != 0, static_cast<hipStream_t>(stream)));
+      fa::launch_exp2_fma(x, y, n, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v,

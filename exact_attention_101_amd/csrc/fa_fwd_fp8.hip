@@ -43,6 +43,7 @@
 // formed and consumed in the same tile, operand fragments read one product
 // ahead, and the row sums of the rounded P from one 16x16x128 MFMA.
 #include "fa_common.h"
+#include "fa_exp2_fma.h"
 
 namespace fa {
 
@@ -161,10 +162,15 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
 //     product runs with neutral scales: it sums the rounded P as formed
 //     (relative to m0 + E) while E stays put, and whenever some row's E
 //     moves the sums are folded into fp32 totals times 2^E first.
-template <bool CAUSAL>
+//   * FMAP (0, 4, 8 or 16) of the 16 exponential pairs a lane forms per
+//     tile run on the FMA pipe (exp2_fma, fa_exp2_fma.h) instead of
+//     v_exp_f32; 0 is the default path.
+template <bool CAUSAL, int FMAP>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const FwdArgs a) {
+  static_assert(FMAP == 0 || FMAP == 4 || FMAP == 8 || FMAP == 16,
+                "FMA-pipe exponential pairs per tile");
   constexpr int NWAVE = 4;
   constexpr int BR = 32 * NWAVE;
   constexpr int NWIN = BT * NCH / (64 * NWAVE);
@@ -367,8 +373,12 @@ fwd_fp8_kernel(const FwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int kb = q >> 3, r = 2 * (q & 7);
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, moff));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, moff));
+      const float x0 = fmaf(s[kb][r], c, moff);
+      const float x1 = fmaf(s[kb][r + 1], c, moff);
+      // Pairs q = 0, 16 / FMAP, 2 * 16 / FMAP, ... on the FMA pipe.
+      const bool on_fma = FMAP > 0 && q % (FMAP > 0 ? 16 / FMAP : 1) == 0;
+      const float e0 = on_fma ? exp2_fma(x0) : __builtin_amdgcn_exp2f(x0);
+      const float e1 = on_fma ? exp2_fma(x1) : __builtin_amdgcn_exp2f(x1);
       pw[q >> 1] = pack_fp8x2(e0, e1, pw[q >> 1], q & 1);
       float& ls = (q & 1) ? ls1 : ls0;
       if (q < 2)
@@ -522,9 +532,33 @@ fwd_fp8_kernel(const FwdArgs a) {
   }
 }
 
+template <int FMAP>
+static void launch_fmap(const FwdArgs& a, bool causal, int grid,
+                        hipStream_t stream) {
+  if (causal) {
+    hipLaunchKernelGGL((fwd_fp8_kernel<true, FMAP>), dim3(grid), dim3(256), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((fwd_fp8_kernel<false, FMAP>), dim3(grid), dim3(256),
+                       0, stream, a);
+  }
+}
+
+// 2^x elementwise by exp2_fma (the FMA-pipe exponential), grid-stride.
+__global__ void __launch_bounds__(256)
+exp2_fma_kernel(const float* x, float* y,
+                long long n) {
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x +
+                     threadIdx.x;
+       i < n; i += stride)
+    y[i] = exp2_fma(x[i]);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
+hipError_t launch_fwd_fp8(FwdArgs a, bool causal, int fma_pairs,
+                          hipStream_t stream) {
   constexpr int BR = 128;
   a.nqb = static_cast<int>((static_cast<long long>(a.N) + BR - 1) / BR);
   const long long grid = static_cast<long long>(a.B) * a.H * a.nqb;
@@ -533,13 +567,23 @@ hipError_t launch_fwd_fp8(FwdArgs a, bool causal, hipStream_t stream) {
     return hipErrorInvalidConfiguration;
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
-  if (causal) {
-    hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3((int)grid),
-                       dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((fwd_fp8_kernel<false>), dim3((int)grid),
-                       dim3(256), 0, stream, a);
+  switch (fma_pairs) {
+    case 0: launch_fmap<0>(a, causal, (int)grid, stream); break;
+    case 4: launch_fmap<4>(a, causal, (int)grid, stream); break;
+    case 8: launch_fmap<8>(a, causal, (int)grid, stream); break;
+    case 16: launch_fmap<16>(a, causal, (int)grid, stream); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_exp2_fma(const float* x, float* y, long long n,
+                           hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(exp2_fma_kernel, dim3(grid), dim3(256), 0, stream, x, y,
+                     n);
   return hipGetLastError();
 }
 

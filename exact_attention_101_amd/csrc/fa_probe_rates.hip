@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include "../../include/fa_probe.h"
+#include "fa_exp2_fma.h"
 
 namespace {
 
@@ -73,6 +74,9 @@ enum Body {
   B_LDS_K = 22,
   B_LDS_V = 23,
   B_LDS_TRSEQ = 24,
+  // The FMA-pipe exponential of the fp8 forward's option (fa_exp2_fma.h):
+  // 16 per round, eight vector instructions each.
+  B_EXP2_FMA = 25,
 };
 
 struct Regs {
@@ -312,6 +316,12 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(v[i]));
     }
+  } else if constexpr (BODY == B_EXP2_FMA) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      r.x[i] = fa::exp2_fma(r.x[i]);
+      asm volatile("" : "+v"(r.x[i]));
+    }
   } else if constexpr (BODY == B_EXP_CHAIN) {
     // The softmax's dependent sequence: scale and shift, exponential, sum.
     // Written with builtins so that the compiler inserts the wait states a
@@ -439,6 +449,7 @@ launch_fn pick_b(int b) {
     case B_MOV64: return launch<A, B_MOV64>;
     case B_CVT16: return launch<A, B_CVT16>;
     case B_CVT8S: return launch<A, B_CVT8S>;
+    case B_EXP2_FMA: return launch<A, B_EXP2_FMA>;
     default: return nullptr;
   }
 }
@@ -476,6 +487,7 @@ launch_fn pick(int a, int b) {
     case B_MOV64: return pick_b<B_MOV64>(b);
     case B_CVT16: return pick_b<B_CVT16>(b);
     case B_CVT8S: return pick_b<B_CVT8S>(b);
+    case B_EXP2_FMA: return pick_b<B_EXP2_FMA>(b);
     case B_MFMA16_ADD: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_DOT2: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;

@@ -111,6 +111,41 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o,
                float scale, const float* descale_qkv, void* stream);
 
 /*
+ * fa_fwd_fp8_exp2_fma -- fa_fwd_fp8 with part of the softmax's
+ * exponentials computed on the FMA pipe instead of the exponential
+ * instruction, the technique of the FlashAttention-4 article
+ * («Оптимизируйте производительность с FlashAttention-4», paragraph 3).
+ * The software 2^x (fa_exp2_fma below) is within 7.5e-5 relative of 2^x.
+ *   fma_pairs  how many of the 16 pairs of weights each lane forms per
+ *              64-key tile use it: 0 (same kernel as fa_fwd_fp8), 4, 8 or
+ *              16; other values give FA_ERR_UNSUPPORTED (checked with d).
+ *   Other arguments, results and accuracy as for fa_fwd_fp8.  On this chip
+ *   the option is slower (eight vector instructions against one
+ *   v_exp_f32, which shares their issue), so fa_fwd_fp8 does not use it.
+ */
+int fa_fwd_fp8_exp2_fma(const void* q8, const void* k8, const void* v8,
+                        void* o, float* lse, int B, int H, int Hkv, int N,
+                        int d, int causal, float scale,
+                        const float* descale_qkv, int fma_pairs,
+                        void* stream);
+
+/*
+ * fa_exp2_fma -- y[i] = 2^x[i] by the FMA-pipe exponential of
+ * fa_fwd_fp8_exp2_fma (the same device function), for testing it.  Range
+ * reduction x = n + f, n = rint(x), f in [-1/2, 1/2] (exact in base 2), a
+ * degree-3 minimax polynomial for 2^f (Remez), 2^n added to the exponent.
+ *   x, y     device float arrays of n elements, 4-byte aligned (x read
+ *            only, y written; they may be the same array).
+ *   n        >= 0 (0 enqueues nothing).
+ *   Accuracy: for -125 <= x <= 127, |y / 2^x - 1| <= 7.5e-5; x < -125
+ *   (-inf included) gives about 2.35e-38 (2^-125 times p(0)) instead of
+ *   a smaller value; x > 127 or NaN is outside the contract.
+ *   Errors: FA_ERR_INVALID_ARGUMENT (null pointer, n < 0),
+ *   FA_ERR_MISALIGNED, FA_ERR_HIP.
+ */
+int fa_exp2_fma(const float* x, float* y, long long n, void* stream);
+
+/*
  * fa_bwd -- gradients of the bf16 forward: dQ, dK, dV for a given dO.
  *   The pages name recomputation as the way FlashAttention avoids storing
  *   the attention matrix (FlashAttention-3 summary, GeekNews, section

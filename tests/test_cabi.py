@@ -81,7 +81,7 @@ def test_probe_library_exports_its_header():
     assert f(18, 1, 8, 1, 8, 1, A, None, None) == 1      # same-wave mix mixed
     assert f(21, 1, 8, 1, 8, 1, A, None, None) == 1      # slot body mixed
     assert f(23, 2, 8, 1, 8, 1, A, None, None) == 1      # LDS body mixed
-    assert f(25, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
+    assert f(26, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
 
 
 def test_version_and_status_strings(lib):
@@ -271,3 +271,32 @@ def test_masked_unsupported_and_alignment(lib):
     assert _mk(lib, mask=A + 2) == fa.FA_ERR_MISALIGNED
     assert _mk(lib, lse=A + 1) == fa.FA_ERR_MISALIGNED
 
+
+
+def test_fp8_exp2_fma_validation(lib):
+    """The fp8 forward with FMA-pipe exponentials checks its arguments like
+    fa_fwd_fp8; fma_pairs other than 0, 4, 8, 16 is unsupported, reported
+    in the same place as an unsupported d."""
+    g = lib.fa_fwd_fp8_exp2_fma
+
+    def call(q=A, N=8, d=128, pairs=8, desc=None):
+        return g(q, A, A, A, A, 1, 2, 2, N, d, 0, 0.1, desc, pairs, None)
+
+    for pairs in (1, 2, 3, 5, 12, 32, -4):
+        assert call(pairs=pairs) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(N=0, pairs=3) == fa.FA_ERR_INVALID_ARGUMENT
+    assert call(q=None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert call(q=M) == fa.FA_ERR_MISALIGNED
+    assert call(desc=A + 2) == fa.FA_ERR_MISALIGNED
+    assert call(q=M, pairs=5) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_exp2_fma_validation(lib):
+    f = lib.fa_exp2_fma
+    assert f(None, A, 4, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert f(A, None, 4, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert f(A, A, -1, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert f(A + 2, A, 4, None) == fa.FA_ERR_MISALIGNED
+    assert f(A, A + 1, 4, None) == fa.FA_ERR_MISALIGNED
+    assert f(A + 4, A + 4, 0, None) == fa.FA_OK        # nothing enqueued
