@@ -84,6 +84,20 @@ int main() {
                     static_cast<const float*>(M4), nullptr),
          FA_ERR_MISALIGNED);
 
+  // ---- fa_fwd_fp8_exp2_fma, fa_exp2_fma ----
+  EXPECT(fa_fwd_fp8_exp2_fma(A, A, A, A, Af, BIG, BIG, BIG, BIG, 128, 1, s,
+                             nullptr, 8, nullptr),
+         FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_fp8_exp2_fma(A, A, A, A, Af, 1, 2, 2, 8, 128, 0, s, nullptr,
+                             BIG, nullptr),
+         FA_ERR_UNSUPPORTED);
+  EXPECT(fa_fwd_fp8_exp2_fma(A, A, A, A, Af, 1, 2, 2, 8, 128, 0, s,
+                             static_cast<const float*>(M4), 4, nullptr),
+         FA_ERR_MISALIGNED);
+  EXPECT(fa_exp2_fma(Af, Af, -1, nullptr), FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_exp2_fma(static_cast<const float*>(M4), Af, LLONG_MAX, nullptr),
+         FA_ERR_MISALIGNED);
+
   // ---- fa_bwd ----
   EXPECT(fa_bwd(A, A, A, A, Af, nullptr, A, A, A, Af, 1, 2, 2, 8, 128, 0, s,
                 nullptr),
