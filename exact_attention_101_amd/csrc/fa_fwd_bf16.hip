@@ -75,6 +75,7 @@
 //     masked score by score only where some row of the wave misses a key.
 #include "fa_common.h"
 
+
 namespace fa {
 
 namespace {
@@ -913,6 +914,11 @@ fwd_bf16_kernel(const FwdArgs a) {
     constexpr bool QK = true;
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr bool NSYNC = decltype(nsync_tag)::value;
+    // Two query blocks: consecutive products share operand A (the two
+    // scores products of a K fragment in even slots, the two P V products
+    // of a V fragment in odd slots) instead of alternating scores and P V
+    // products; measured 1.1-1.8% faster (same GPU, bit-identical).
+    constexpr bool PAIRED = NQB == 2 && PV && QK;
     // SYNC steps start the copies of tiles (blk-1)/2 + 2 (K, into kw) and
     // (blk-1)/2 + 1 (V, into vw), one per issue slot from slot 1 on, so
     // that their issue overlaps the matrix work; their descriptors are
@@ -951,13 +957,35 @@ fwd_bf16_kernel(const FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
-      // Each slot: scores MFMA, then p = exp2(S c - m) for PPS pairs while
-      // it runs; P V MFMA, then the bf16 packs and lane sums of those pairs
-      // while that one runs.  With one wave per SIMD, this keeps vector work
-      // under both MFMAs and puts the exp latency between the two halves.
-      if constexpr (QK) {
-        // k-step i / NQB for query block i % NQB: the fragment serves all.
-        const int f = i / NQB, qb = i % NQB;
+      // Each slot: an MFMA, then p = exp2(S c - m) for PPS pairs while it
+      // runs; a second MFMA, then the bf16 packs and lane sums of those
+      // pairs while that one runs.  With one wave per SIMD, this keeps
+      // vector work under both MFMAs and puts the exp latency between the
+      // two halves.  The two MFMAs are a scores and a P V product, or
+      // (PAIRED) the two scores products of a K fragment (even slots) or
+      // the two P V products of a V fragment (odd slots).
+      if constexpr (PAIRED) {
+        // Odd slot: first P V product of V fragment i / 2 (query block 0),
+        // with that fragment's read-ahead replaced (this step's stage, or
+        // the next step's, whose barrier came in slot NSL - 4).
+        if (i % 2 == 1) {
+          const int f = i / 2;
+          vcur[0] = vf[f % VPF][0];
+          vcur[1] = vf[f % VPF][1];
+          if (f + VPF < NVF) {
+            vf[f % VPF][0] = vread(vr, VH, f + VPF, 0);
+            vf[f % VPF][1] = vread(vr, VH, f + VPF, 1);
+          } else {
+            vf[f % VPF][0] = vread(vrn, VHN, f + VPF - NVF, 0);
+            vf[f % VPF][1] = vread(vrn, VHN, f + VPF - NVF, 1);
+          }
+          mfma_pv(vcur, pp[0][f / G::NDB], oacc[0][f % G::NDB]);
+        }
+      }
+      if (QK && (!PAIRED || i % 2 == 0)) {
+        // k-step i / NQB for query block i % NQB: the fragment serves all
+        // (PAIRED: k-step i / 2, query block 0; block 1 follows below).
+        const int f = i / NQB, qb = PAIRED ? 0 : i % NQB;
         if (qb == 0) {
           kcur = kf[f % KPF];
           if (f + KPF < G::NKS) kf[f % KPF] = kfrag(kr, KH, f + KPF);
@@ -1015,7 +1043,15 @@ fwd_bf16_kernel(const FwdArgs a) {
         asm volatile("" : "+v"(e[q][0]), "+v"(e[q][1]));
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (PV) {
+      if constexpr (PAIRED) {
+        // Second product of the slot: the same operand A as the first.
+        const int f = i / 2;
+        if (i % 2 == 0)
+          sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(kcur), qf[1][f], sn[1], 0, 0, 0);
+        else
+          mfma_pv(vcur, pp[1][f / G::NDB], oacc[1][f % G::NDB]);
+      } else if constexpr (PV) {
         // V fragment i / NQB = (db, u) for query block i % NQB.
         const int f = i / NQB, qb = i % NQB;
         if (qb == 0) {
@@ -1028,7 +1064,7 @@ fwd_bf16_kernel(const FwdArgs a) {
         }
         mfma_pv(vcur, pp[qb][f / G::NDB], oacc[qb][f % G::NDB]);
       }
-      {
+      if constexpr (!PAIRED) {
         // Read-ahead into the next step, which always has a P V product
         // (after the barrier above when the next step is a SYNC step).
         const int f = i / NQB, qb = i % NQB;
