@@ -40,6 +40,8 @@ struct FwdArgs {
   float scale;            // signed scale (fp8 path folds descales into it)
   int neg;                // scale < 0: Q is negated on load so that c >= 0
   int xcd_chunk;          // 1: map workgroups to XCD-contiguous work ranges
+  int persist;            // dense non-causal forward: workgroups loop over
+                          // the B * H * nqb units (grid < units)
   // Variable-length / windowed launches only (unused otherwise): sequence b
   // owns query rows [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1])
   // of tensors packed per head; window widths (-1 = unbounded).

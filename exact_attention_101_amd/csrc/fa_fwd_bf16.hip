@@ -75,6 +75,10 @@
 //     masked score by score only where some row of the wave misses a key.
 #include "fa_common.h"
 
+#ifndef FA_PERSIST
+#define FA_PERSIST 1
+#endif
+
 
 namespace fa {
 
@@ -217,7 +221,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc,
 template <int D, bool CAUSAL, int NQB, bool VL = false, bool MK = false,
           int NW = 8 / NQB>
 __global__ void __launch_bounds__((Waves<NQB, NW>::NTHR), 1)
-fwd_bf16_kernel(const FwdArgs a) {
+fwd_bf16_kernel(const FwdArgs a_arg) {
   constexpr int NWAVE = Waves<NQB, NW>::NWAVE;
   constexpr int QPW = Waves<NQB, NW>::QPW;
   constexpr int BR = Waves<NQB, NW>::BR;
@@ -245,6 +249,28 @@ fwd_bf16_kernel(const FwdArgs a) {
   const int li = lane & 31;             // MFMA column / row-in-block
   const int h = lane >> 5;              // lane half
 
+  // Work units: (batch, head, query block), one per workgroup, except in
+  // the persistent launch of the dense non-causal forward (a.persist: N a
+  // multiple of BR, one workgroup per CU), where a workgroup takes units
+  // blockIdx.x, blockIdx.x + gridDim.x, ... (all of equal work).  There the
+  // last copy steps of a unit copy the next unit's first K and V tiles into
+  // the stages its prologue would fill, and the next unit's Q loads are
+  // issued before this unit's epilogue, so the next unit starts without
+  // waiting for memory (and without a workgroup launch).
+  constexpr bool PS = !CAUSAL && !VL && !MK;
+  const int nunits = PS && a_arg.persist ? a_arg.B * a_arg.H * a_arg.nqb
+                                         : static_cast<int>(gridDim.x);
+  uint4 qraw[NQB][G::NKS];              // Q of the unit, as loaded
+  bool have = false;                    // its Q loads and first tiles issued
+  // (One trip, known at compile time, unless PS.)
+  for (int unit = blockIdx.x, trip = 0; PS ? unit < nunits : trip < 1;
+       unit += static_cast<int>(gridDim.x), ++trip) {
+  // The arguments are read again for every unit (scalar-cache hits), so
+  // that none of them is held in a register across the main loop.
+  typedef const __attribute__((address_space(4))) FwdArgs KArgs;
+  KArgs* ap = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+  if constexpr (PS) asm volatile("" : "+s"(ap));
+  KArgs& a = *ap;
   int bh, qblk;
   if constexpr (VL) {
     // Sequences differ in length, so no XCD may own whole sequences:
@@ -253,7 +279,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     // K and V in that XCD's L2), longest-running query blocks first.  With
     // Hkv not a multiple of 8, consecutive workgroups take consecutive
     // (sequence, head) pairs.
-    const int L = blockIdx.x;
+    const int L = unit;
     if (a.xcd_chunk) {
       const int x = L & 7;
       int t = L >> 3;
@@ -270,8 +296,7 @@ fwd_bf16_kernel(const FwdArgs a) {
       qblk = a.nqb - 1 - L / (a.B * a.H);
     }
   } else {
-    map_work(blockIdx.x, gridDim.x, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh,
-             qblk);
+    map_work(unit, nunits, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh, qblk);
   }
   const int b = bh / a.H;
   const int hq = bh % a.H;
@@ -338,15 +363,38 @@ fwd_bf16_kernel(const FwdArgs a) {
   // issued (below), so the Q loads and the copies wait together once,
   // instead of each load waiting in turn.
   bf16x8_t qf[NQB][G::NKS];
-  uint4 qraw[NQB][G::NKS];
+  // Q rows qwx + 32 j + li (j < NQB) of the nq rows at qpx.
+  auto load_q = [&](const uint16_t* qpx, int qwx, int nq) {
 #pragma unroll
-  for (int j = 0; j < NQB; ++j) {
-    const int row = qw0 + 32 * j + li;
-    const bool ok = row < NQ;
-    const uint16_t* src = qp + static_cast<int64_t>(ok ? row : NQ - 1) * D +
-                          h * (D / 2);
+    for (int j = 0; j < NQB; ++j) {
+      const int row = qwx + 32 * j + li;
+      const bool ok = row < nq;
+      const uint16_t* src = qpx + static_cast<int64_t>(ok ? row : nq - 1) * D +
+                            h * (D / 2);
 #pragma unroll
-    for (int s = 0; s < G::NKS; ++s) qraw[j][s] = keep_if(ldg16(src + 8 * s), ok);
+      for (int s = 0; s < G::NKS; ++s)
+        qraw[j][s] = keep_if(ldg16(src + 8 * s), ok);
+    }
+  };
+  if (!have) load_q(qp, qw0, NQ);
+
+  // PS: the next unit's Q, K and V (null when there is none).
+  const uint16_t* nqp = nullptr;
+  const uint16_t* nkp = nullptr;
+  const uint16_t* nvp = nullptr;
+  if constexpr (PS) {
+    const int nu = unit + static_cast<int>(gridDim.x);
+    if (nu < nunits) {
+      int bh2, qb2;
+      map_work(nu, nunits, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh2, qb2);
+      const int b2 = bh2 / a.H;
+      const int hk2 = (bh2 % a.H) / a.group;
+      nqp = static_cast<const uint16_t*>(a.q) +
+            (static_cast<int64_t>(bh2) * a.N + qb2 * BR) * D;
+      const int64_t k2 = (static_cast<int64_t>(b2) * a.Hkv + hk2) * a.N * D;
+      nkp = static_cast<const uint16_t*>(a.k) + k2;
+      nvp = static_cast<const uint16_t*>(a.v) + k2;
+    }
   }
   auto settle_q = [&]() {
     const uint32_t flip = a.neg ? 0x80008000u : 0u;
@@ -592,6 +640,13 @@ fwd_bf16_kernel(const FwdArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(base + static_cast<int64_t>(kv0) * D), 0,
         rows * D * 2, 0x00020000);
+  };
+  // PS: tiles past this unit's last key are the next unit's first tiles
+  // (same N, so kv0 - kv_end is their first key).
+  auto rsrc_kv = [&](const uint16_t* base, const uint16_t* nbase, int kv0) {
+    if (PS && nbase != nullptr && kv0 >= kv_end)
+      return rsrc_at(nbase, kv0 - kv_end);
+    return rsrc_at(base, kv0);
   };
   auto copy_k = [&](int tile, const uint4* stage) {
     const auto rs = rsrc_at(kp, tkv(tile));
@@ -1008,8 +1063,8 @@ fwd_bf16_kernel(const FwdArgs a) {
             rk = rsrc_at(kp, kvk);
             rv = rsrc_at(vp, tkv(tile + 1));
           } else {
-            rk = rsrc_at(kp, tkv(tile + 2));
-            rv = rsrc_at(vp, tkv(tile + 1));
+            rk = rsrc_kv(kp, nkp, tkv(tile + 2));
+            rv = rsrc_kv(vp, nvp, tkv(tile + 1));
           }
         }
         if constexpr (SERIAL_COPIES) {
@@ -1134,9 +1189,11 @@ fwd_bf16_kernel(const FwdArgs a) {
   //   blk%4 == 1: K Ks1 half 0, V Vs0 half 0, SYNC: fill Vs1, Ks0
   //   blk%4 == 2: K Ks1 half 1, V Vs0 half 1
   //   blk%4 == 3: K Ks0 half 0, V Vs1 half 0, SYNC: fill Vs0, Ks1
-  copy_k(0, Ks0);
-  copy_v(0, Vs0);
-  copy_k(1, Ks1);
+  if (!have) {
+    copy_k(0, Ks0);
+    copy_v(0, Vs0);
+    copy_k(1, Ks1);
+  }
   settle_q();
   wait_copies_and_sync(-1);
   f32x16_t s[NQB];
@@ -1195,6 +1252,16 @@ fwd_bf16_kernel(const FwdArgs a) {
          Int<1>{}, Int<0>{}, Int<0>{}, T0{}, T1{}, T1{}, Int<0>{});
   }
 
+  // PS: the next unit's first tiles are in the stages (the last step waited
+  // for every copy); its Q loads go out before this unit's epilogue.
+  have = false;
+  if constexpr (PS) {
+    if (nqp != nullptr) {
+      load_q(nqp, wave * QPW, BR);
+      have = true;
+    }
+  }
+
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
   acc_read_fence();
 #pragma unroll
@@ -1227,9 +1294,25 @@ fwd_bf16_kernel(const FwdArgs a) {
       }
     }
   }
+  }  // units
 }
 
 }  // namespace
+
+// Compute units of the current device (0 if it cannot be read), read once
+// per device.
+static int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                              dev) == hipSuccess)
+      cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // 64 rows per wave, one wave per SIMD (halves LDS reads per FLOP against
 // 32-row waves; the single wave per SIMD is issue-bound but still ahead):
@@ -1294,12 +1377,24 @@ hipError_t launch_fwd_bf16(FwdArgs a, int d, bool causal, hipStream_t stream) {
     return hipErrorInvalidConfiguration;
   const int bh = a.B * a.H;
   a.xcd_chunk = causal ? (bh % 8 == 0) : (grid % 8 == 0);
-  if (d == 64) {
-    return causal ? launch<64, true>(a, (int)grid, stream)
-                  : launch<64, false>(a, (int)grid, stream);
+  // Persistent launch (one workgroup per CU looping over the units): dense
+  // non-causal, every unit whole (N a multiple of BR), more units than CUs,
+  // and a CU count that keeps each workgroup on one XCD's units.
+  int g = static_cast<int>(grid);
+  a.persist = 0;
+  if (FA_PERSIST && !causal && a.N % BR == 0) {
+    const int ncu = cu_count();
+    if (ncu > 0 && ncu % 8 == 0 && ncu < grid) {
+      a.persist = 1;
+      g = ncu;
+    }
   }
-  return causal ? launch<128, true>(a, (int)grid, stream)
-                : launch<128, false>(a, (int)grid, stream);
+  if (d == 64) {
+    return causal ? launch<64, true>(a, g, stream)
+                  : launch<64, false>(a, g, stream);
+  }
+  return causal ? launch<128, true>(a, g, stream)
+                : launch<128, false>(a, g, stream);
 }
 
 }  // namespace fa

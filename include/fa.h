@@ -22,7 +22,9 @@
  *   - Device pointers are HIP device allocations owned by the caller.  The
  *     library never allocates or frees device memory and never synchronises
  *     the device; calls are thread-safe.  The only global state is the
- *     fixed per-device scratch of fa_fwd_splitkv_noalloc (see there).
+ *     fixed per-device scratch of fa_fwd_splitkv_noalloc (see there) and a
+ *     per-device cache of the compute-unit count (read once, used to size
+ *     the persistent launch of the dense non-causal forward).
  *   - Layouts are dense row-major:  q, o: [B][H][N][d];  k, v: [B][Hkv][N][d];
  *     lse: [B][H][N] (float, natural log).  All offsets are 64-bit.
  *   - Grouped-query attention: H must be a multiple of Hkv; query head h

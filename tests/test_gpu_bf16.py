@@ -217,3 +217,32 @@ def test_rising_scores_move_the_reference(d, causal):
     ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb),
                               causal=causal, scale=scale)
     _check(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_persistent_launch_uneven_units(d):
+    """Dense non-causal shapes with more 256-row units than compute units
+    run one workgroup per CU looping over units (600 units here, so some
+    workgroups take three and the rest two), each unit's first tiles copied
+    by the previous unit and its Q loaded before that unit's epilogue.
+    Grouped heads (4 query heads per KV head), every output compared."""
+    q, k, v = workloads.qkv(3, 100, 25, 512, d, 4242)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    o, lse = _run(*tb, False)
+    ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb))
+    _check(o, lse, ro, rl)
+
+
+def test_persistent_launch_moving_reference():
+    """The persistent launch with the reference moving inside every unit
+    (rising key norms, large scale): each unit starts from a fresh running
+    maximum, sum and output."""
+    q, k, v = workloads.qkv(1, 80, 80, 1024, 128, 4343)
+    ramp = np.linspace(0.25, 4.0, 1024, dtype=np.float32)[None, None, :, None]
+    k = (k * ramp).astype(np.float32)
+    tb = [workloads.to_bf16(x) for x in (q, k, v)]
+    scale = 4.0 / math.sqrt(128)
+    o, lse = _run(*tb, False, scale=scale)
+    ro, rl = oracle.attention(*(workloads.bf16_values(t) for t in tb),
+                              scale=scale)
+    _check(o, lse, ro, rl)
