@@ -193,6 +193,11 @@ PROBE_BODIES = {
     "exp2_fma": (25, 16, "the FMA-pipe exponential of the fp8 forward's "
                          "option (8 vector instructions; counted per "
                          "exponential)"),
+    "slot_bf16_pipelined": (26, 4, "the same issue slot with its vector "
+                                   "work pipelined across slots (fma of "
+                                   "pair i+1 and exp of pair i after the "
+                                   "first MFMA, pack and sums of pair i-1 "
+                                   "after the second; counted per slot)"),
 }
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
@@ -211,7 +216,8 @@ PROBE_CONFIGS = (
                                           "dot2_bf16", "mov_b64")]
     + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
     + [("mfma_f8", "exp2_fma", 8, 1), ("mfma_bf16", "exp2_fma", 8, 1)]
-    + [("slot_bf16", "idle", 4 * n, n) for n in (1, 2)]
+    + [(b, "idle", 4 * n, n) for n in (1, 2)
+       for b in ("slot_bf16", "slot_bf16_pipelined")]
     + [(b, "idle", 4 * n, n) for n in (1, 2, 4)
        for b in ("lds_k", "lds_v", "lds_tr_seq")]
 )

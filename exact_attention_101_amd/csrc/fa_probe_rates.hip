@@ -77,6 +77,11 @@ enum Body {
   // The FMA-pipe exponential of the fp8 forward's option (fa_exp2_fma.h):
   // 16 per round, eight vector instructions each.
   B_EXP2_FMA = 25,
+  // The same issue slot with the vector work pipelined across slots: the
+  // FMAs of pair i + 1 and the exponentials of pair i follow the first
+  // MFMA, the pack and sums of pair i - 1 the second, so no vector
+  // instruction waits for a result of its own slot.
+  B_SLOT16P = 26,
 };
 
 struct Regs {
@@ -88,6 +93,7 @@ struct Regs {
   i32x8_t da[2], db[2];     // data operands (B_MFMA*_DATA)
   float lsum;               // B_SLOT16 lane sum
   float cs;                 // B_SLOT16 scale (uniform)
+  float px0, px1, pe0, pe1; // B_SLOT16P values carried between slots
   const uint8_t* lds;       // B_LDS_*: the workgroup's LDS reserve
 };
 
@@ -271,6 +277,35 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
       asm volatile("" : "+v"(r.w[j]), "+v"(r.lsum));
       __builtin_amdgcn_sched_barrier(0);
     }
+  } else if constexpr (BODY == B_SLOT16P) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float cs = r.cs;
+      asm volatile("" : "+s"(cs));
+      __builtin_amdgcn_sched_barrier(0);
+      r.acc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a16, a16, r.acc[j & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const float nx0 = fmaf(r.x[(2 * j + 2) & 15], cs, -r.z);
+      const float nx1 = fmaf(r.x[(2 * j + 3) & 15], cs, -r.z);
+      const float e0 = __builtin_amdgcn_exp2f(r.px0);
+      const float e1 = __builtin_amdgcn_exp2f(r.px1);
+      asm volatile("" : "+v"(r.acc[j & 1]));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(r.acc[2 + (j & 1)])
+                   : "v"(a16), "v"(a16));
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x2_t pk = {static_cast<__bf16>(r.pe0), static_cast<__bf16>(r.pe1)};
+      r.w[j] = __builtin_bit_cast(int, pk);
+      r.lsum += r.pe0 + r.pe1;
+      asm volatile("" : "+v"(r.w[j]), "+v"(r.lsum));
+      __builtin_amdgcn_sched_barrier(0);
+      r.px0 = nx0;
+      r.px1 = nx1;
+      r.pe0 = e0;
+      r.pe1 = e1;
+    }
   } else if constexpr (BODY == B_LDS_K || BODY == B_LDS_V ||
                        BODY == B_LDS_TRSEQ) {
     typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
@@ -364,6 +399,7 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   r.dsrc = seed;
   r.lsum = 0.f;
   r.cs = 0.999f;
+  r.px0 = r.px1 = r.pe0 = r.pe1 = seed;
   r.lds = reinterpret_cast<const uint8_t*>(reserve);
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
@@ -401,7 +437,7 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   for (int i = 0; i < 8; ++i) sink += static_cast<float>(r.dd[i]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) sink += r.acc[j][lane & 15];
-  sink += r.lsum;
+  sink += r.lsum + r.px0 + r.px1 + r.pe0 + r.pe1;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     sink += static_cast<float>(r.da[j][lane & 7] ^ r.db[j][lane & 7]);
@@ -463,6 +499,7 @@ launch_fn pick_alone(int a) {
     case B_MFMA16_DOT2: return launch<B_MFMA16_DOT2, B_IDLE>;
     case B_MFMA16_MOV64: return launch<B_MFMA16_MOV64, B_IDLE>;
     case B_SLOT16: return launch<B_SLOT16, B_IDLE>;
+    case B_SLOT16P: return launch<B_SLOT16P, B_IDLE>;
     case B_LDS_K: return launch<B_LDS_K, B_IDLE>;
     case B_LDS_V: return launch<B_LDS_V, B_IDLE>;
     case B_LDS_TRSEQ: return launch<B_LDS_TRSEQ, B_IDLE>;
@@ -492,6 +529,7 @@ launch_fn pick(int a, int b) {
     case B_MFMA16_DOT2: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_SLOT16:
+    case B_SLOT16P:
     case B_LDS_K:
     case B_LDS_V:
     case B_LDS_TRSEQ: return b == B_IDLE ? pick_alone(a) : nullptr;

@@ -36,8 +36,11 @@ extern "C" {
  *           ds_read_b64_tr_b16 at its V fragment addresses, 24
  *           ds_read_b64_tr_b16 at consecutive 8-byte units, 25 the
  *           FMA-pipe exponential of fa_fwd_fp8_exp2_fma (16 per round,
- *           eight vector instructions each); b may also be 0, idle, and
- *           must be for bodies 12, 13, 17 to 19 and 21 to 24).
+ *           eight vector instructions each), 26 body 21 with its vector
+ *           work pipelined across slots (the FMAs of pair i + 1 and the
+ *           exponentials of pair i after the first MFMA, the pack and
+ *           sums of pair i - 1 after the second); b may also be 0, idle,
+ *           and must be for bodies 12, 13, 17 to 19, 21 to 24 and 26).
  *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
  *           CU, so waves / 4 waves on each SIMD; bodies 22 to 24 read the
  *           workgroup's 96 KiB LDS reserve, shared by its waves).
