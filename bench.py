@@ -198,7 +198,16 @@ PROBE_BODIES = {
                                    "pair i+1 and exp of pair i after the "
                                    "first MFMA, pack and sums of pair i-1 "
                                    "after the second; counted per slot)"),
+    "lds_dma_copy": (27, 16, "buffer_load_dwordx4 ... lds, 1 KB per wave, "
+                             "from an L2-resident 16 KB buffer"),
+    "mfma_bf16+copy": (28, 4, "bf16 MFMA, each followed by one LDS-DMA "
+                              "copy (counted per MFMA)"),
+    "slot_bf16+copy": (29, 4, "the bf16 forward's issue slot with one "
+                              "LDS-DMA copy after its first MFMA (counted "
+                              "per slot)"),
 }
+# Bodies that copy from (or multiply) the caller's data buffer.
+PROBE_DATA_BODIES = (12, 13, 27, 28, 29)
 
 # (body A, body B, waves per workgroup, A waves per SIMD): one workgroup per
 # CU, four waves per SIMD at most (the SIMD of each wave is read from its
@@ -217,7 +226,8 @@ PROBE_CONFIGS = (
     + [("mfma_f8", "exp+fma", 12, 1), ("mfma_f8", "exp_chain", 12, 1)]
     + [("mfma_f8", "exp2_fma", 8, 1), ("mfma_bf16", "exp2_fma", 8, 1)]
     + [(b, "idle", 4 * n, n) for n in (1, 2)
-       for b in ("slot_bf16", "slot_bf16_pipelined")]
+       for b in ("slot_bf16", "slot_bf16_pipelined", "lds_dma_copy",
+                 "mfma_bf16+copy", "slot_bf16+copy")]
     + [(b, "idle", 4 * n, n) for n in (1, 2, 4)
        for b in ("lds_k", "lds_v", "lds_tr_seq")]
 )
@@ -240,14 +250,17 @@ def _rates(iters: int) -> dict:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream().cuda_stream
     rows = []
+    # 16 KB of N(0, 1) values: the copy source of the LDS-DMA bodies.
+    data = torch.randn(4096, device="cuda:0").contiguous()
     for a, b, waves, na in PROBE_CONFIGS:
         out = torch.zeros(cus * waves * 3, dtype=torch.int64, device="cuda:0")
         ia, na_i, _ = PROBE_BODIES[a]
         ib, nb_i, _ = PROBE_BODIES[b]
+        dptr = data.data_ptr() if ia in PROBE_DATA_BODIES else None
         runs = []
         for rep in range(4):              # the first run warms the clock
             rc = lib.fa_probe_rates(ia, ib, waves, na, iters, cus,
-                                    out.data_ptr(), None, stream)
+                                    out.data_ptr(), dptr, stream)
             if rc != 0:
                 raise RuntimeError(f"fa_probe_rates({a}, {b}) = {rc}")
             torch.cuda.synchronize()

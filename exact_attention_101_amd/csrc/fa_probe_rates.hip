@@ -82,6 +82,15 @@ enum Body {
   // MFMA, the pack and sums of pair i - 1 the second, so no vector
   // instruction waits for a result of its own slot.
   B_SLOT16P = 26,
+  // LDS-DMA tile copies (buffer_load_dwordx4 ... lds, 1 KB per wave each)
+  // from the caller's 16 KB buffer (L2-resident) into a 1 KB slice of the
+  // workgroup's LDS reserve, at most 8 left in flight after each round:
+  // 16 copies alone, 4 x (bf16 MFMA + copy), and the bf16 slot (body 21)
+  // with a copy after its first MFMA, as the forward's copy steps issue
+  // them.
+  B_COPY = 27,
+  B_MFMA16_COPY = 28,
+  B_SLOT16_COPY = 29,
 };
 
 struct Regs {
@@ -95,6 +104,8 @@ struct Regs {
   float cs;                 // B_SLOT16 scale (uniform)
   float px0, px1, pe0, pe1; // B_SLOT16P values carried between slots
   const uint8_t* lds;       // B_LDS_*: the workgroup's LDS reserve
+  __amdgpu_buffer_rsrc_t src;  // B_*COPY: the caller's 16 KB buffer
+  float* dst;                  // B_*COPY: this wave's 1 KB of LDS
 };
 
 __device__ __forceinline__ void fma16(Regs& r, int first, int n) {
@@ -277,6 +288,54 @@ __device__ __forceinline__ void round_of(Regs& r, const i32x8_t& a8,
       asm volatile("" : "+v"(r.w[j]), "+v"(r.lsum));
       __builtin_amdgcn_sched_barrier(0);
     }
+  } else if constexpr (BODY == B_SLOT16_COPY) {
+    // Phases fenced as in the forward kernel; the scale is an opaque
+    // scalar, so the FMAs read fixed inputs without being hoisted.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float cs = r.cs;
+      asm volatile("" : "+s"(cs));
+      __builtin_amdgcn_sched_barrier(0);
+      r.acc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a16, a16, r.acc[j & 1], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r.src, (__attribute__((address_space(3))) void*)(r.dst), 16,
+          16 * (threadIdx.x & 63), 1024 * j, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(r.x[2 * j], cs, -r.z));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(r.x[2 * j + 1], cs, -r.z));
+      asm volatile("" : "+v"(r.acc[j & 1]));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(r.acc[2 + (j & 1)])
+                   : "v"(a16), "v"(a16));
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x2_t pk = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+      r.w[j] = __builtin_bit_cast(int, pk);
+      r.lsum += e0 + e1;
+      asm volatile("" : "+v"(r.w[j]), "+v"(r.lsum));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  } else if constexpr (BODY == B_COPY) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r.src, (__attribute__((address_space(3))) void*)(r.dst), 16,
+          16 * (threadIdx.x & 63), 1024 * j, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  } else if constexpr (BODY == B_MFMA16_COPY) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a16, a16, r.acc[j],
+                                                         0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r.src, (__attribute__((address_space(3))) void*)(r.dst), 16,
+          16 * (threadIdx.x & 63), 1024 * j, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
   } else if constexpr (BODY == B_SLOT16P) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -401,6 +460,9 @@ __global__ void __launch_bounds__(1024) probe_kernel(unsigned long long* out,
   r.cs = 0.999f;
   r.px0 = r.px1 = r.pe0 = r.pe1 = seed;
   r.lds = reinterpret_cast<const uint8_t*>(reserve);
+  r.src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<i32x8_t*>(data), 0, data ? 16384 : 0, 0x00020000);
+  r.dst = reserve + 256 * __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.acc[j] = f32x16_t{};
   // Data operands: lane-dependent fragments of the caller's 512-entry
@@ -500,6 +562,9 @@ launch_fn pick_alone(int a) {
     case B_MFMA16_MOV64: return launch<B_MFMA16_MOV64, B_IDLE>;
     case B_SLOT16: return launch<B_SLOT16, B_IDLE>;
     case B_SLOT16P: return launch<B_SLOT16P, B_IDLE>;
+    case B_COPY: return launch<B_COPY, B_IDLE>;
+    case B_MFMA16_COPY: return launch<B_MFMA16_COPY, B_IDLE>;
+    case B_SLOT16_COPY: return launch<B_SLOT16_COPY, B_IDLE>;
     case B_LDS_K: return launch<B_LDS_K, B_IDLE>;
     case B_LDS_V: return launch<B_LDS_V, B_IDLE>;
     case B_LDS_TRSEQ: return launch<B_LDS_TRSEQ, B_IDLE>;
@@ -530,6 +595,9 @@ launch_fn pick(int a, int b) {
     case B_MFMA16_MOV64: return b == B_IDLE ? pick_alone(a) : nullptr;
     case B_SLOT16:
     case B_SLOT16P:
+    case B_COPY:
+    case B_MFMA16_COPY:
+    case B_SLOT16_COPY:
     case B_LDS_K:
     case B_LDS_V:
     case B_LDS_TRSEQ: return b == B_IDLE ? pick_alone(a) : nullptr;
@@ -575,7 +643,8 @@ extern "C" __attribute__((visibility("default"))) int fa_probe_rates(
   if (!out || waves < 4 || waves > 16 || waves % 4 != 0 || na < 0 ||
       na > waves / 4 || iters < 1 || grid < 1)
     return 1;
-  if ((a == B_MFMA16_DATA || a == B_MFMA8_DATA) &&
+  if ((a == B_MFMA16_DATA || a == B_MFMA8_DATA || a == B_COPY ||
+       a == B_MFMA16_COPY || a == B_SLOT16_COPY) &&
       (!data || (reinterpret_cast<uintptr_t>(data) & 31u)))
     return 1;
   const launch_fn f = pick(a, b);

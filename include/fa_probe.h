@@ -39,8 +39,13 @@ extern "C" {
  *           eight vector instructions each), 26 body 21 with its vector
  *           work pipelined across slots (the FMAs of pair i + 1 and the
  *           exponentials of pair i after the first MFMA, the pack and
- *           sums of pair i - 1 after the second); b may also be 0, idle,
- *           and must be for bodies 12, 13, 17 to 19, 21 to 24 and 26).
+ *           sums of pair i - 1 after the second), 27 16 LDS-DMA tile
+ *           copies (buffer_load_dwordx4 ... lds, 1 KB each) from `data`
+ *           into the wave's slice of the LDS reserve, 28 4 x (bf16 MFMA +
+ *           one such copy), 29 body 21 with one such copy after its first
+ *           MFMA (27 to 29 leave at most 8 copies in flight per round); b
+ *           may also be 0, idle, and must be for bodies 12, 13, 17 to 19
+ *           and 21 to 29).
  *   waves   waves per workgroup, 4..16, a multiple of 4 (one workgroup per
  *           CU, so waves / 4 waves on each SIMD; bodies 22 to 24 read the
  *           workgroup's 96 KiB LDS reserve, shared by its waves).
@@ -53,8 +58,8 @@ extern "C" {
  *           the wave's HW_ID register (SIMD in bits 5:4).
  *   data    device, 512 entries of 32 bytes, 32-byte aligned (read only):
  *           operand values of bodies 12 and 13 (lane l, fragment j reads
- *           entries (l + 64 j) % 512 and (l + 64 j + 256) % 512); may be
- *           NULL for the other bodies.
+ *           entries (l + 64 j) % 512 and (l + 64 j + 256) % 512) and the
+ *           copy source of bodies 27 to 29; may be NULL for the others.
  *   stream  hipStream_t or NULL; one kernel is enqueued.
  *   Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the
  *   launch failed.

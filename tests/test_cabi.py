@@ -81,7 +81,8 @@ def test_probe_library_exports_its_header():
     assert f(18, 1, 8, 1, 8, 1, A, None, None) == 1      # same-wave mix mixed
     assert f(21, 1, 8, 1, 8, 1, A, None, None) == 1      # slot body mixed
     assert f(23, 2, 8, 1, 8, 1, A, None, None) == 1      # LDS body mixed
-    assert f(27, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
+    assert f(30, 0, 4, 1, 8, 1, A, None, None) == 1      # past the last body
+    assert f(27, 0, 4, 1, 8, 1, A, None, None) == 1      # copy body, no data
     assert f(26, 1, 8, 1, 8, 1, A, None, None) == 1      # slot body mixed
 
 
