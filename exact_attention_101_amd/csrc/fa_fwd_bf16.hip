@@ -243,11 +243,8 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
   __shared__ uint32_t tfp[MK ? NTL / 32 : 1];
   __shared__ int tl_n[1];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-  const int li = lane & 31;             // MFMA column / row-in-block
-  const int h = lane >> 5;              // lane half
+  const int tid0 = threadIdx.x;
+  const int wave0 = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // uniform
 
   // Work units: (batch, head, query block), one per workgroup, except in
   // the persistent launch of the dense non-causal forward (a.persist: N a
@@ -271,6 +268,17 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
   KArgs* ap = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
   if constexpr (PS) asm volatile("" : "+s"(ap));
   KArgs& a = *ap;
+  // PS: the lane index is also taken again for every unit, so that the
+  // per-lane offsets derived from it are formed per unit instead of being
+  // held (and spilled) across the unit loop.
+  int tid = tid0;
+  if constexpr (PS)
+    tid = 64 * wave0 +
+          __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int lane = tid & 63;
+  const int wave = wave0;
+  const int li = lane & 31;             // MFMA column / row-in-block
+  const int h = lane >> 5;              // lane half
   int bh, qblk;
   if constexpr (VL) {
     // Sequences differ in length, so no XCD may own whole sequences:
@@ -378,24 +386,25 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
   };
   if (!have) load_q(qp, qw0, NQ);
 
-  // PS: the next unit's Q, K and V (null when there is none).
-  const uint16_t* nqp = nullptr;
-  const uint16_t* nkp = nullptr;
-  const uint16_t* nvp = nullptr;
-  if constexpr (PS) {
-    const int nu = unit + static_cast<int>(gridDim.x);
-    if (nu < nunits) {
-      int bh2, qb2;
-      map_work(nu, nunits, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh2, qb2);
-      const int b2 = bh2 / a.H;
-      const int hk2 = (bh2 % a.H) / a.group;
-      nqp = static_cast<const uint16_t*>(a.q) +
-            (static_cast<int64_t>(bh2) * a.N + qb2 * BR) * D;
-      const int64_t k2 = (static_cast<int64_t>(b2) * a.Hkv + hk2) * a.N * D;
-      nkp = static_cast<const uint16_t*>(a.k) + k2;
-      nvp = static_cast<const uint16_t*>(a.v) + k2;
-    }
-  }
+  // PS: the next unit's Q rows, K and V (false when there is none).  The
+  // unit index is taken opaquely, so that this is formed where it is used
+  // (the last copy steps, the loop's end) and not held across the loop.
+  auto next_unit = [&](const uint16_t*& nq, const uint16_t*& nk,
+                       const uint16_t*& nv) {
+    int nu = unit + static_cast<int>(gridDim.x);
+    asm volatile("" : "+s"(nu));
+    if (nu >= nunits) return false;
+    int bh2, qb2;
+    map_work(nu, nunits, a.B * a.H, a.nqb, CAUSAL, a.xcd_chunk, bh2, qb2);
+    const int b2 = bh2 / a.H;
+    const int hk2 = (bh2 % a.H) / a.group;
+    nq = static_cast<const uint16_t*>(a.q) +
+         (static_cast<int64_t>(bh2) * a.N + qb2 * BR) * D;
+    const int64_t k2 = (static_cast<int64_t>(b2) * a.Hkv + hk2) * a.N * D;
+    nk = static_cast<const uint16_t*>(a.k) + k2;
+    nv = static_cast<const uint16_t*>(a.v) + k2;
+    return true;
+  };
   auto settle_q = [&]() {
     const uint32_t flip = a.neg ? 0x80008000u : 0u;
 #pragma unroll
@@ -643,9 +652,16 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
   };
   // PS: tiles past this unit's last key are the next unit's first tiles
   // (same N, so kv0 - kv_end is their first key).
-  auto rsrc_kv = [&](const uint16_t* base, const uint16_t* nbase, int kv0) {
-    if (PS && nbase != nullptr && kv0 >= kv_end)
-      return rsrc_at(nbase, kv0 - kv_end);
+  // The next unit's K and V (null when there is none), formed once.
+  const uint16_t* nkp = nullptr;
+  const uint16_t* nvp = nullptr;
+  if constexpr (PS) {
+    const uint16_t* nq;
+    if (!next_unit(nq, nkp, nvp)) nkp = nvp = nullptr;
+  }
+  auto rsrc_kv = [&](const uint16_t* base, bool is_v, int kv0) {
+    if (PS && nkp != nullptr && kv0 >= kv_end)
+      return rsrc_at(is_v ? nvp : nkp, kv0 - kv_end);
     return rsrc_at(base, kv0);
   };
   auto copy_k = [&](int tile, const uint4* stage) {
@@ -1061,10 +1077,10 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
             kvk = tkv(tile + 2);
             fullk = tfull(tile + 2);
             rk = rsrc_at(kp, kvk);
-            rv = rsrc_at(vp, tkv(tile + 1));
+            rv = rsrc_kv(vp, true, tkv(tile + 1));
           } else {
-            rk = rsrc_kv(kp, nkp, tkv(tile + 2));
-            rv = rsrc_kv(vp, nvp, tkv(tile + 1));
+            rk = rsrc_kv(kp, false, tkv(tile + 2));
+            rv = rsrc_kv(vp, true, tkv(tile + 1));
           }
         }
         if constexpr (SERIAL_COPIES) {
@@ -1256,12 +1272,20 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
   // for every copy); its Q loads go out before this unit's epilogue.
   have = false;
   if constexpr (PS) {
-    if (nqp != nullptr) {
-      load_q(nqp, wave * QPW, BR);
+    const uint16_t *nq, *nk, *nv;
+    if (next_unit(nq, nk, nv)) {
+      load_q(nq, wave * QPW, BR);
       have = true;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQB; ++j)
+#pragma unroll
+        for (int t = 0; t < G::NKS; ++t) qraw[j][t] = make_uint4(0, 0, 0, 0);
     }
   }
 
+  // PS: the output offsets are formed here, not held across the loop.
+  if constexpr (PS) asm volatile("" : "+s"(qrow0));
   // ---- epilogue: O / l in bf16 (RNE), LSE in natural log ----
   acc_read_fence();
 #pragma unroll
