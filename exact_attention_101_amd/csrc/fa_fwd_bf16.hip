@@ -75,6 +75,10 @@
 //     masked score by score only where some row of the wave misses a key.
 #include "fa_common.h"
 
+#ifndef FA_PAIR1
+#define FA_PAIR1 1
+#endif
+
 #ifndef FA_PERSIST
 #define FA_PERSIST 1
 #endif
@@ -990,6 +994,12 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
     // of a V fragment in odd slots) instead of alternating scores and P V
     // products; measured 1.1-1.8% faster (same GPU, bit-identical).
     constexpr bool PAIRED = NQB == 2 && PV && QK;
+    // One query block (32-row waves: the variable-length and masked
+    // configurations): even slots issue the scores products of two
+    // consecutive K fragments, odd slots the P V products of two
+    // consecutive V fragments (which share operand B, P of the same 16
+    // keys); measured 0.6-2.3% faster on those launches, bit-identical.
+    constexpr bool PAIR1 = FA_PAIR1 != 0 && NQB == 1 && PV && QK;
     // SYNC steps start the copies of tiles (blk-1)/2 + 2 (K, into kw) and
     // (blk-1)/2 + 1 (V, into vw), one per issue slot from slot 1 on, so
     // that their issue overlaps the matrix work; their descriptors are
@@ -1023,8 +1033,8 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
     // Lane sums of the even / odd pairs of each query block, started by its
     // first two pairs (8 j and 8 j + 1).
     float lse_[NQB], lso_[NQB];
-    uint4 kcur = {};
-    i16x4_t vcur[2] = {};
+    uint4 kcur = {}, kcur2 = {};
+    i16x4_t vcur[2] = {}, vcur2[2] = {};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
@@ -1034,7 +1044,47 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
       // vector work under both MFMAs and puts the exp latency between the
       // two halves.  The two MFMAs are a scores and a P V product, or
       // (PAIRED) the two scores products of a K fragment (even slots) or
-      // the two P V products of a V fragment (odd slots).
+      // the two P V products of a V fragment (odd slots), or (PAIR1) two
+      // scores products (even slots) or two P V products (odd slots) of
+      // consecutive fragments.
+      if constexpr (PAIR1) {
+        const int f = i & ~1;             // first of the slot's two fragments
+        if (i % 2 == 0) {
+          kcur = kf[0];
+          kcur2 = kf[1];
+          if (f + 2 < G::NKS) {
+            kf[0] = kfrag(kr, KH, f + 2);
+            kf[1] = kfrag(kr, KH, f + 3);
+          } else {
+            // First reads of the next step's stage; every read of this
+            // step's stages is issued.
+            if (NSYNC) wait_copies_and_sync(blk / 2 + 2);
+            kf[0] = kfrag(krn, KHN, 0);
+            kf[1] = kfrag(krn, KHN, 1);
+          }
+          sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(kcur), qf[0][f], sn[0], 0, 0, 0);
+        } else {
+          vcur[0] = vf[0][0];
+          vcur[1] = vf[0][1];
+          vcur2[0] = vf[1][0];
+          vcur2[1] = vf[1][1];
+          if (f + 2 < NVF) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              vf[t][0] = vread(vr, VH, f + 2 + t, 0);
+              vf[t][1] = vread(vr, VH, f + 2 + t, 1);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              vf[t][0] = vread(vrn, VHN, t, 0);
+              vf[t][1] = vread(vrn, VHN, t, 1);
+            }
+          }
+          mfma_pv(vcur, pp[0][f / G::NDB], oacc[0][f % G::NDB]);
+        }
+      }
       if constexpr (PAIRED) {
         // Odd slot: first P V product of V fragment i / 2 (query block 0),
         // with that fragment's read-ahead replaced (this step's stage, or
@@ -1053,7 +1103,7 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
           mfma_pv(vcur, pp[0][f / G::NDB], oacc[0][f % G::NDB]);
         }
       }
-      if (QK && (!PAIRED || i % 2 == 0)) {
+      if (QK && !PAIR1 && (!PAIRED || i % 2 == 0)) {
         // k-step i / NQB for query block i % NQB: the fragment serves all
         // (PAIRED: k-step i / 2, query block 0; block 1 follows below).
         const int f = i / NQB, qb = PAIRED ? 0 : i % NQB;
@@ -1114,7 +1164,14 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
         asm volatile("" : "+v"(e[q][0]), "+v"(e[q][1]));
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (PAIRED) {
+      if constexpr (PAIR1) {
+        const int f = i & ~1;
+        if (i % 2 == 0)
+          sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(kcur2), qf[0][f + 1], sn[0], 0, 0, 0);
+        else
+          mfma_pv(vcur2, pp[0][(f + 1) / G::NDB], oacc[0][(f + 1) % G::NDB]);
+      } else if constexpr (PAIRED) {
         // Second product of the slot: the same operand A as the first.
         const int f = i / 2;
         if (i % 2 == 0)
@@ -1135,7 +1192,7 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
         }
         mfma_pv(vcur, pp[qb][f / G::NDB], oacc[qb][f % G::NDB]);
       }
-      if constexpr (!PAIRED) {
+      if constexpr (!PAIRED && !PAIR1) {
         // Read-ahead into the next step, which always has a P V product
         // (after the barrier above when the next step is a SYNC step).
         const int f = i / NQB, qb = i % NQB;
