@@ -204,7 +204,6 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
   const int k0 = kb * BLK;
   const int kw0 = k0 + T * wave;
   const int key = kw0 + li;
-  const bool kok = key < N;
 
   const int64_t khead = (static_cast<int64_t>(b) * a.Hkv + hk) * N;
   bf16x8_t kf[8], vf[8];
@@ -326,10 +325,16 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_kernel(const BwdArgs a) {
     if (step + 1 < nsteps) run(step + 1, s1, s0);
   }
 
-  if (kok) {
-    const int64_t off = (khead + key) * static_cast<int64_t>(D);
-    store_rows(static_cast<uint16_t*>(a.dk) + off, dk, a.scale, h);
-    store_rows(static_cast<uint16_t*>(a.dv) + off, dv, 1.f, h);
+  // The lane's key is formed again from the lane count rather than held
+  // across the loop, which needs every vector register (held, it was
+  // spilled to memory).
+  const int elane =
+      __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ekey = kw0 + (elane & 31);
+  if (ekey < N) {
+    const int64_t off = (khead + ekey) * static_cast<int64_t>(D);
+    store_rows(static_cast<uint16_t*>(a.dk) + off, dk, a.scale, elane >> 5);
+    store_rows(static_cast<uint16_t*>(a.dv) + off, dv, 1.f, elane >> 5);
   }
 }
 
