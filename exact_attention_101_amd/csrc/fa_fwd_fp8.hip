@@ -370,6 +370,12 @@ fwd_fp8_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" : "=v"(pw[i]));
     float ls0, ls1;
+    // The softmax's vector work is what bounds a tile (see above): while a
+    // wave is in it, its instructions go before the other waves' (whose
+    // matrix instructions need few issue cycles); measured 1.0-1.4% faster
+    // than equal priorities, and 1% slower with the priority on the matrix
+    // instructions instead.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int kb = q >> 3, r = 2 * (q & 7);
@@ -390,6 +396,7 @@ fwd_fp8_kernel(const FwdArgs a) {
       asm volatile("" : "+v"(pw[q >> 1]), "+v"(ls));
     }
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(0);
     const i32x8_t pp = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     const int eb = 127 + e_cur;
     const i32x8_t ones = {one, one, one, one, one, one, one, one};
