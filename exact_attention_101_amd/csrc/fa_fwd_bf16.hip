@@ -1152,6 +1152,10 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      // VL (two waves per SIMD): a wave in its exponentials, packs and sums
+      // issues before the other one; measured 0.7-1.3% faster than equal
+      // priorities (and within noise on the masked configuration).
+      if constexpr (VL) __builtin_amdgcn_s_setprio(1);
       float e[PPS][2];
 #pragma unroll
       for (int q = 0; q < PPS; ++q) {
@@ -1215,6 +1219,7 @@ fwd_bf16_kernel(const FwdArgs a_arg) {
           acc += p0 + p1;
         asm volatile("" : "+v"(w[pr]), "+v"(acc));
       }
+      if constexpr (VL) __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Accept P of block blk or take the exact step first, then add it to l.
